@@ -1,0 +1,103 @@
+"""Integer oracle for the workgroup-ID -> (batch, head, row block) remap.
+
+TEST INFRASTRUCTURE ONLY (same rule as oracle/sdpa.py): only tests/,
+``__graft_entry__.smoke()`` and bench.py's cpu_baseline leg may use it.  It is
+pure Python and shares no code with the C++ header the kernel uses.
+
+Source: "Optimizing Attention on GPUs by Exploiting GPU Architectural NUMA
+Effects" (digest page).
+
+* §2 Q1: the hardware dispatcher hands linear workgroup id w to XCD
+  ``w mod X`` (chunked round-robin with chunk 1).
+* §2 Q2 and §3 Figure 10: an Attention Compute Cluster (ACC) is the set of
+  workgroups that read the same K/V, i.e. one head for MHA and one KV group for
+  GQA; Swizzled Head-first puts every workgroup of one ACC on one XCD and lets
+  each XCD work on one ACC at a time.
+* §3 "Method as before/after diff" and §5: the baselines are Naive
+  Block-first (all heads of a row block before the next block), Naive
+  Head-first (all blocks of a head before the next head, no swizzle) and
+  Swizzled Block-first (block-first order behind the chiplet swizzle of §7,
+  Figure 3).
+* §7 Figure 11 gives Swizzled Head-first for one batch with H_Q a multiple of
+  X; §7 "key implementation details" says the pages define no fallback.
+
+Readings (the pages are silent or their printed form is not a bijection):
+
+* Batch is the outermost index of the logical order: L = b·(H_Q·M) + r.
+* Block-first decode of r: m = r // H_Q, h = r mod H_Q (heads fastest).
+* Head-first decode of r: h = r // M, m = r mod M (blocks fastest).  With
+  contiguous GQA groups this order is ACC-major: ACC (b, kv) owns the
+  contiguous range [(b·H_Q + kv·G)·M, +G·M).
+* Chiplet swizzle: XCD x = w mod X receives the w's congruent to x in
+  increasing order, and gets the x-th contiguous slice of the logical order.
+  Slices differ in length by at most one when X does not divide W (the
+  printed swizzle divides W by X and is a bijection only when X | W):
+  sigma(w) = x·floor(W/X) + min(x, W mod X) + floor(w/X).
+  This balanced split is the fallback when the number of ACCs is not a
+  multiple of X: every XCD still takes the ACCs in one contiguous run, and
+  an ACC is split between neighbouring XCDs only where a slice boundary falls
+  inside it.
+
+Parity status: pinned.  On the domain where the pages print formulas (one
+batch, X dividing H_Q, X dividing W) tests/test_wg_map_oracle.py checks
+equality with those formulas restated from the pages, and the invariants the
+pages state (one ACC per XCD, 16 heads per XCD for Naive Block-first at
+H_Q=128, Figure 10's 8-head / 4-XCD example) everywhere else.
+"""
+from __future__ import annotations
+
+NBF, NHF, SBF, SHF = 0, 1, 2, 3
+MODE_NAMES = {NBF: "naive_block_first", NHF: "naive_head_first",
+              SBF: "swizzled_block_first", SHF: "swizzled_head_first"}
+
+
+def row_blocks(N: int, block_m: int = 128) -> int:
+    """Row blocks per head, M = ceil(N / BLOCK_M) (BLOCK_M = 128, §4)."""
+    return -(-N // block_m)
+
+
+def num_workgroups(B: int, H_Q: int, N: int, block_m: int = 128) -> int:
+    return B * H_Q * row_blocks(N, block_m)
+
+
+def xcd_of(w: int, X: int) -> int:
+    """XCD that the chunk-1 round-robin dispatcher gives workgroup w."""
+    return w % X
+
+
+def chiplet_swizzle(w: int, W: int, X: int) -> int:
+    """Logical index of workgroup w: XCD x owns the x-th contiguous slice."""
+    x = w % X
+    return x * (W // X) + min(x, W % X) + w // X
+
+
+def _decode(L: int, H_Q: int, M: int, head_first: bool):
+    per_batch = H_Q * M
+    b, r = divmod(L, per_batch)
+    if head_first:
+        h, m = divmod(r, M)
+    else:
+        m, h = divmod(r, H_Q)
+    return b, h, m
+
+
+def wg_map(mode: int, w: int, B: int, H_Q: int, N: int, X: int,
+           block_m: int = 128):
+    """(b, h_q, m) computed by linear workgroup id ``w`` under ``mode``."""
+    M = row_blocks(N, block_m)
+    W = B * H_Q * M
+    if not 0 <= w < W:
+        raise ValueError("workgroup id out of range")
+    if mode in (SBF, SHF):
+        L = chiplet_swizzle(w, W, X)
+    elif mode in (NBF, NHF):
+        L = w
+    else:
+        raise ValueError("unknown mapping mode")
+    return _decode(L, H_Q, M, head_first=mode in (NHF, SHF))
+
+
+def wg_table(mode: int, B: int, H_Q: int, N: int, X: int, block_m: int = 128):
+    """List of (b, h, m) for w = 0..W-1."""
+    W = num_workgroups(B, H_Q, N, block_m)
+    return [wg_map(mode, w, B, H_Q, N, X, block_m) for w in range(W)]

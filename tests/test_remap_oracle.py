@@ -1,0 +1,215 @@
+"""The integer remap oracle against the pages' formulas and invariants (CPU).
+
+Formulas restated from "Optimizing Attention on GPUs by Exploiting GPU
+Architectural NUMA Effects" (digest page):
+* §2 Q2 / §7 Figure 11 (Swizzled Head-first, one batch, X | H_Q):
+  head  = (w mod X) * (H_Q / X) + floor(w / (X * M))
+  block = floor((w mod (X * M)) / X)
+* §7 Figure 3 (chiplet swizzle, X | W):
+  new_id = (w mod X) * (W / X) + floor(w / X)
+"""
+import os
+import random
+from collections import defaultdict
+
+import pytest
+
+import oracle
+from oracle import NBF, NHF, SBF, SHF
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+# (B, H_Q, H_KV, N) of every workload the forward pass is measured on.
+CONFIGS = [
+    (1, 8, 8, 1024),
+    (1, 128, 128, 8192), (1, 128, 128, 32768), (1, 128, 128, 131072),
+    (1, 64, 8, 8192), (1, 64, 8, 32768), (1, 64, 8, 131072),
+    (2, 32, 4, 32768), (2, 12, 12, 32768), (1, 12, 12, 32768),
+]
+
+
+def pages_shf(w, H_Q, M, X):
+    return (w % X) * (H_Q // X) + w // (X * M), (w % (X * M)) // X
+
+
+def pages_swizzle(w, W, X):
+    return (w % X) * (W // X) + w // X
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([int(x) for x in line.split()])
+    return rows
+
+
+def _random_shapes(n, seed=0):
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        H_KV = rng.randint(1, 10)
+        G = rng.randint(1, 4)
+        B = rng.randint(1, 4)
+        M = rng.randint(1, 20)
+        N = M * 128 - rng.choice([0, 0, 1, 64, 127])
+        X = rng.choice([1, 2, 4, 8])
+        out.append((B, H_KV * G, H_KV, max(N, 1), X))
+    return out
+
+
+@pytest.mark.parametrize("mode", [NBF, NHF, SBF, SHF])
+def test_every_mode_is_a_bijection(mode):
+    shapes = [(B, H_Q, H_KV, N, 8) for B, H_Q, H_KV, N in CONFIGS]
+    shapes += _random_shapes(200)
+    for B, H_Q, H_KV, N, X in shapes:
+        M = oracle.row_blocks(N)
+        tab = oracle.wg_table(mode, B, H_Q, N, X)
+        assert len(tab) == B * H_Q * M
+        assert len(set(tab)) == len(tab), (mode, B, H_Q, N, X)
+        for b, h, m in tab:
+            assert 0 <= b < B and 0 <= h < H_Q and 0 <= m < M
+
+
+def test_shf_equals_pages_formula_single_batch():
+    for H_Q, M, X in [(128, 64, 8), (16, 8, 8), (64, 3, 8), (8, 128, 4),
+                      (128, 1024, 8), (24, 5, 4), (6, 7, 2), (5, 9, 1)]:
+        for w in range(H_Q * M):
+            b, h, m = oracle.wg_map(SHF, w, 1, H_Q, M * 128, X)
+            assert b == 0 and (h, m) == pages_shf(w, H_Q, M, X), (H_Q, M, X, w)
+
+
+def test_sbf_equals_pages_swizzle_then_block_first():
+    for B, H_Q, M, X in [(1, 128, 64, 8), (2, 16, 8, 8), (1, 12, 2, 8),
+                         (3, 4, 2, 4), (1, 8, 128, 4)]:
+        W = B * H_Q * M
+        assert W % X == 0
+        for w in range(W):
+            L = pages_swizzle(w, W, X)
+            b, r = divmod(L, H_Q * M)
+            expect = (b, r % H_Q, r // H_Q)
+            assert oracle.wg_map(SBF, w, B, H_Q, M * 128, X) == expect
+
+
+def _acc(b, h, H_Q, H_KV):
+    return b * H_KV + h // (H_Q // H_KV)
+
+
+def _xcd_runs(mode, B, H_Q, H_KV, N, X):
+    """Per XCD: the ACC of each workgroup in dispatch order."""
+    W = oracle.num_workgroups(B, H_Q, N)
+    per = defaultdict(list)
+    for w in range(W):
+        b, h, _ = oracle.wg_map(mode, w, B, H_Q, N, X)
+        per[oracle.xcd_of(w, X)].append(_acc(b, h, H_Q, H_KV))
+    return per
+
+
+def test_shf_puts_each_acc_on_one_xcd_one_at_a_time():
+    shapes = [(B, H_Q, H_KV, N, 8) for B, H_Q, H_KV, N in CONFIGS]
+    shapes += [s for s in _random_shapes(300, seed=1)]
+    checked = 0
+    for B, H_Q, H_KV, N, X in shapes:
+        if (B * H_KV) % X:
+            continue
+        checked += 1
+        per = _xcd_runs(SHF, B, H_Q, H_KV, N, X)
+        owner = {}
+        for x, accs in per.items():
+            assert accs == sorted(accs), "an XCD must finish one ACC before the next"
+            assert len(set(accs)) == B * H_KV // X
+            for a in set(accs):
+                assert owner.setdefault(a, x) == x, "ACC split over XCDs"
+        assert len(owner) == B * H_KV
+    assert checked > 30
+
+
+def test_fallback_is_balanced_and_contiguous():
+    shapes = [(1, 12, 12, 32768, 8), (1, 32, 4, 32768, 8), (1, 8, 1, 8192, 8),
+              (3, 5, 5, 1000, 8), (1, 2, 1, 300, 8)]
+    shapes += [s for s in _random_shapes(300, seed=2)]
+    checked = 0
+    for B, H_Q, H_KV, N, X in shapes:
+        if (B * H_KV) % X == 0:
+            continue
+        checked += 1
+        W = oracle.num_workgroups(B, H_Q, N)
+        per = _xcd_runs(SHF, B, H_Q, H_KV, N, X)
+        sizes = [len(per.get(x, [])) for x in range(X)]
+        assert max(sizes) - min(sizes) <= 1
+        U = (H_Q // H_KV) * oracle.row_blocks(N)
+        slice_len = W // X
+        spans = defaultdict(set)
+        for x, accs in per.items():
+            assert accs == sorted(accs)
+            for a in accs:
+                spans[a].add(x)
+        for a, xs in spans.items():
+            xs = sorted(xs)
+            assert xs == list(range(xs[0], xs[-1] + 1)), "ACC on non-adjacent XCDs"
+            if slice_len:
+                assert len(xs) <= -(-U // slice_len) + 1
+    assert checked > 30
+
+
+def test_fallback_c4_prime_split():
+    """B=1, H=12, X=8: 12 ACCs of 256 blocks over 8 slices of 384 blocks:
+    8 ACCs stay whole and 4 are split over two XCDs."""
+    per = _xcd_runs(SHF, 1, 12, 12, 32768, 8)
+    spans = defaultdict(set)
+    for x, accs in per.items():
+        for a in accs:
+            spans[a].add(x)
+    n_split = sum(1 for xs in spans.values() if len(xs) == 2)
+    assert n_split == 4 and all(len(xs) <= 2 for xs in spans.values())
+
+
+def test_naive_block_first_16_heads_per_xcd_golden():
+    golden = _read_golden("nbf_h128_heads_per_xcd.txt")
+    for N in (128, 1024, 131072):
+        per = _xcd_runs(NBF, 1, 128, 128, N, 8)
+        got = sorted((x, len(set(a))) for x, a in per.items())
+        assert [list(t) for t in got] == golden
+
+
+def test_naive_head_first_stripes_a_head_over_xcds():
+    for B, H_Q, N, X in [(1, 128, 131072, 8), (1, 8, 1024, 8), (1, 4, 384, 8),
+                         (2, 3, 640, 4)]:
+        M = oracle.row_blocks(N)
+        W = B * H_Q * M
+        seen = defaultdict(set)
+        for w in range(W):
+            b, h, _ = oracle.wg_map(NHF, w, B, H_Q, N, X)
+            seen[(b, h)].add(oracle.xcd_of(w, X))
+        assert all(len(s) == min(X, M) for s in seen.values())
+
+
+def test_figure10_worked_example_golden():
+    golden = _read_golden("fig10_shf_x4_h8_m128.txt")
+    N = 128 * 128
+    count = defaultdict(lambda: defaultdict(int))
+    for w in range(8 * 128):
+        b, h, m = oracle.wg_map(SHF, w, 1, 8, N, 4)
+        count[h][oracle.xcd_of(w, 4)] += 1
+    got = []
+    for h in range(8):
+        (x, c), = count[h].items()
+        got.append([h, x, c])
+    assert got == golden
+
+
+def test_printed_batch_term_needs_the_batch_outer_reading():
+    """As printed, the per-batch id is the linear id divided by the batch
+    count; with two batches that is not a bijection, which is why the oracle
+    puts the batch outermost."""
+    B, H_Q, M, X = 2, 16, 8, 8
+    seen = set()
+    for w in range(B * H_Q * M):
+        wpb = w // B
+        head = (wpb % X) * (H_Q // X) + wpb // (X * M)
+        block = (wpb % (X * M)) // X
+        batch = (w // (M * H_Q)) % B
+        seen.add((batch, head, block))
+    assert len(seen) < B * H_Q * M
