@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Attention forward benchmark on one MI355X: TFLOP/s, fraction of the bf16
+MFMA peak and L2 hit rate for each workgroup mapping mode.
+
+One step = one attention forward pass (one kernel launch) over the workload's
+synthetic inputs, which are resident in HBM before timing starts.  Default
+workload: MHA, B=1, H_Q=H_KV=128, N=131072, d=128, non-causal, bf16 N(0,1)
+inputs.  Every mapping mode is timed in turn; the headline value is Swizzled
+Head-first.  Prints ONE JSON line on stdout (progress goes to stderr).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--modes 0,1,2,3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["chiplet_numa_aware_amd/csrc/attn_fwd_kernel.hpp",
+                  "chiplet_numa_aware_amd/csrc/wg_map.hpp",
+                  "chiplet_numa_aware_amd/csrc/attn_numa.hip"]
+
+METRIC = "attn fwd TFLOP/s + % bf16 MFMA peak + L2 hit %, MHA H=128 N=128K d=128"
+# MI355X published dense bf16 MFMA peak (2.5 PFLOP/s).
+PEAK_BF16_TFLOPS = 2500.0
+MODE_NAMES = ["naive_block_first", "naive_head_first",
+              "swizzled_block_first", "swizzled_head_first"]
+
+WORKLOADS = {
+    # name: (B, H_Q, H_KV, N, d, causal)
+    "mha_128k": (1, 128, 128, 131072, 128, False),
+    "mha_128k_causal": (1, 128, 128, 131072, 128, True),
+    "mha_32k": (1, 128, 128, 32768, 128, False),
+    "mha_32k_causal": (1, 128, 128, 32768, 128, True),
+    "mha_8k": (1, 128, 128, 8192, 128, False),
+    "mha_8k_causal": (1, 128, 128, 8192, 128, True),
+    "gqa64x8_128k_causal": (1, 64, 8, 131072, 128, True),
+    "gqa64x8_32k_causal": (1, 64, 8, 32768, 128, True),
+    "gqa64x8_8k_causal": (1, 64, 8, 8192, 128, True),
+    "gqa32x4_b2_32k_causal": (2, 32, 4, 32768, 128, True),
+    "mha12_b2_32k_causal": (2, 12, 12, 32768, 128, True),
+    "mha12_b1_32k_causal": (1, 12, 12, 32768, 128, True),
+    "dsv3_d56_128k_causal": (1, 128, 128, 131072, 56, True),
+    "dsv3_d56_32k_causal": (1, 128, 128, 32768, 56, True),
+    "mha_h8_1k": (1, 8, 8, 1024, 128, False),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_flops(B, H_Q, N, d, causal) -> float:
+    """Algorithmic FLOPs: QK^T and PV, 2*d each per (query, visible key)."""
+    pairs = N * (N + 1) // 2 if causal else N * N
+    return 4.0 * B * H_Q * d * pairs
+
+
+def describe(name) -> str:
+    B, H_Q, H_KV, N, d, causal = WORKLOADS[name]
+    kind = "MHA" if H_Q == H_KV else "GQA"
+    return (f"{kind} fwd B={B} H_Q={H_Q} H_KV={H_KV} N={N} d={d} "
+            f"{'causal' if causal else 'non-causal'}")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_counters(workload: str, khash: str):
+    """Counter-derived figures (L2 hit, HBM bytes) kept under profiles/ for
+    this workload, or None when absent or taken on another kernel version."""
+    path = os.path.join(PROFILES, f"counters_attn_fwd_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("kernel_hash") != khash:
+        return None
+    return data
+
+
+def time_mode(attn, q, k, v, o, lse, causal, mode, steps, warmup, flops):
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        attn.attn_fwd(q, k, v, causal=causal, mapping=mode, o=o, lse=lse,
+                      stream=stream)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        attn.attn_fwd(q, k, v, causal=causal, mapping=mode, o=o, lse=lse,
+                      stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_kernel_s = sum(kern_ms) / len(kern_ms) / 1e3
+    return {
+        "ms_per_step": wall / steps * 1e3,
+        "tflops": flops / (wall / steps) / 1e12,
+        "kernel_ms_avg": avg_kernel_s * 1e3,
+        "kernel_ms_min": min(kern_ms),
+        "kernel_tflops": flops / avg_kernel_s / 1e12,
+        "pct_peak": 100.0 * flops / avg_kernel_s / 1e12 / PEAK_BF16_TFLOPS,
+    }
+
+
+def cpu_baseline(q, k, v, causal, budget_s: float):
+    """The fp64 oracle timed on this host on sampled rows of the workload."""
+    import numpy as np
+    import oracle  # the cpu_baseline leg is the one place bench.py uses it
+    from chiplet_numa_aware_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity size
+        threads = len(os.sched_getaffinity(0))
+    B, H_Q, N, d = q.shape
+    H_KV = k.shape[1]
+    rows_per_pair = 256
+    samples = inputs.sample_rows(B, H_Q, H_KV, N, n_pairs=16,
+                                 n_rows=rows_per_pair, seed=1234)
+    done_flops, done_s, pairs = 0.0, 0.0, 0
+    for b, h, rows in samples:
+        g = oracle.kv_head(h, H_Q, H_KV)
+        qh = q[b, h].float().cpu().numpy()[rows]
+        kh = k[b, g].float().cpu().numpy()
+        vh = v[b, g].float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.attention_head_rows(qh, kh, vh, rows, causal)
+        done_s += time.perf_counter() - t0
+        allowed = (rows + 1) if causal else np.full(len(rows), N)
+        done_flops += float(4.0 * d * allowed.sum())
+        pairs += 1
+        if done_s >= budget_s:
+            break
+    return {
+        "value": done_flops / done_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{pairs} (batch, head) pairs x {rows_per_pair} query rows "
+                   f"of the workload (seed 1234), fp64 numpy, "
+                   f"{done_flops / 1e9:.1f} GFLOP in {done_s:.1f} s"),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="mha_128k", choices=sorted(WORKLOADS))
+    ap.add_argument("--modes", default="0,1,2,3",
+                    help="mapping modes to time; the last one listed that is "
+                         "3 (or the last one) is the headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the attention forward pass here runs "
+              "on a single MI355X; multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chiplet_numa_aware_amd as attn
+    from chiplet_numa_aware_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    attn.load_library()
+    B, H_Q, H_KV, N, d, causal = WORKLOADS[args.workload]
+    modes = [int(m) for m in args.modes.split(",") if m.strip() != ""]
+    headline = 3 if 3 in modes else modes[-1]
+    flops = attn_flops(B, H_Q, N, d, causal)
+    log(f"workload {describe(args.workload)}: {flops / 1e12:.1f} TFLOP per call")
+
+    q, k, v = inputs.make_qkv(B, H_Q, H_KV, N, d, seed=1000, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H_Q, N), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    results = {}
+    for mode in modes:
+        r = time_mode(attn, q, k, v, o, lse, causal, mode, args.steps,
+                      args.warmup, flops)
+        results[mode] = r
+        log(f"  {MODE_NAMES[mode]:22s} {r['tflops']:8.1f} TFLOP/s "
+            f"({r['pct_peak']:.1f}% of peak, kernel {r['kernel_ms_avg']:.2f} ms)")
+
+    khash = kernel_hash()
+    counters = stored_counters(args.workload, khash)
+    head = results[headline]
+    modes_out = {}
+    for mode, r in results.items():
+        entry = {k2: round(v2, 4) for k2, v2 in r.items()}
+        if counters and MODE_NAMES[mode] in counters.get("modes", {}):
+            c = counters["modes"][MODE_NAMES[mode]]
+            entry["l2_hit_pct"] = c.get("l2_hit_pct")
+            entry["hbm_bytes_per_launch"] = c.get("hbm_bytes")
+        modes_out[MODE_NAMES[mode]] = entry
+
+    traffic = None
+    l2_hit = None
+    if counters and MODE_NAMES[headline] in counters.get("modes", {}):
+        c = counters["modes"][MODE_NAMES[headline]]
+        traffic = c.get("hbm_bytes")
+        l2_hit = c.get("l2_hit_pct")
+
+    out = {
+        "metric": METRIC,
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: bf16 N(0,1) Q/K/V from fixed seeds",
+        "config": {
+            "workload": describe(args.workload),
+            "B": B, "H_Q": H_Q, "H_KV": H_KV, "N": N, "d": d,
+            "causal": causal, "mapping": MODE_NAMES[headline],
+            "block_m": 128, "parallelism": "single GPU",
+        },
+        "pct_peak": round(head["pct_peak"], 2),
+        "l2_hit_pct": l2_hit,
+        "modes": modes_out,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(head["kernel_tflops"], 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(head["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "kernel_hash": khash,
+    }
+    if 0 in results and headline in results and headline != 0:
+        out["speedup_vs_naive_block_first"] = round(
+            results[0]["kernel_ms_avg"] / results[headline]["kernel_ms_avg"], 4)
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host (cpu_baseline)")
+        out["cpu_baseline"] = cpu_baseline(q, k, v, causal, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

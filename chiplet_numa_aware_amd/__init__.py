@@ -1,0 +1,178 @@
+"""Python binding of libattn_numa (NUMA-aware attention forward for MI355X).
+
+Argument marshalling only: every step of the attention forward pass runs in
+the library's HIP kernels.  torch provides device memory and streams.  The
+entry points have the names of the C ABI in include/attn_numa.h:
+
+* ``attn_fwd(q, k, v, causal=False, mapping=3, o=None, lse=None)``
+* ``attn_wg_map(mapping, B, H_Q, H_KV, N, num_xcd)``
+* ``attn_num_xcd()``
+* ``attn_probe_placement(mapping, B, H_Q, H_KV, N, out=None)``
+* ``attn_strerror(code)``
+
+The library must be built (``python -m chiplet_numa_aware_amd.build``);
+there is no fallback: a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch  # first, so the library binds to the HIP runtime torch loaded
+
+__all__ = [
+    "AttnError", "attn_fwd", "attn_wg_map", "attn_num_xcd",
+    "attn_probe_placement", "attn_strerror", "library_path", "load_library",
+    "MAPPINGS", "row_blocks", "num_workgroups", "BLOCK_M",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "libattn_numa.so")
+BLOCK_M = 128
+
+# Mapping modes (ATTN_MAP_* in include/attn_numa.h).
+MAPPINGS = {
+    "naive_block_first": 0,
+    "naive_head_first": 1,
+    "swizzled_block_first": 2,
+    "swizzled_head_first": 3,
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {attn_strerror(code)} (code {code})")
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Loads libattn_numa.so and declares its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m chiplet_numa_aware_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp] + [i32] * 7 + [vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_wg_map.argtypes = [i32] * 6 + [vp]
+    lib.attn_wg_map.restype = i32
+    lib.attn_num_xcd.argtypes = []
+    lib.attn_num_xcd.restype = i32
+    lib.attn_probe_placement.argtypes = [i32] * 5 + [vp, vp]
+    lib.attn_probe_placement.restype = i32
+    lib.attn_strerror.argtypes = [i32]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_strerror(code: int) -> str:
+    return load_library().attn_strerror(int(code)).decode()
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise AttnError(code, where)
+
+
+def row_blocks(N: int) -> int:
+    return -(-N // BLOCK_M)
+
+
+def num_workgroups(B: int, H_Q: int, N: int) -> int:
+    return B * H_Q * row_blocks(N)
+
+
+def _mapping_id(mapping) -> int:
+    if isinstance(mapping, str):
+        return MAPPINGS[mapping]
+    return int(mapping)
+
+
+def _stream_handle(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+             causal: bool = False, mapping=3, o: torch.Tensor | None = None,
+             lse: torch.Tensor | None = None, need_lse: bool = True,
+             stream: torch.cuda.Stream | None = None):
+    """Attention forward on the GPU: returns (o, lse).
+
+    q [B,H_Q,N,d], k and v [B,H_KV,N,d]: contiguous bf16 on one GPU.  o and
+    lse are allocated when not given (lse is None when need_lse is False and
+    no lse is given).  Enqueued on ``stream`` (default: torch's current
+    stream); returns without synchronising.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D tensor")
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 GPU tensor")
+    B, H_Q, N, d = q.shape
+    H_KV = k.shape[1]
+    if k.shape != (B, H_KV, N, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H_KV, N, d] with q's B, N, d")
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous():
+        raise ValueError("o must be a contiguous bf16 tensor shaped like q")
+    if lse is None and need_lse:
+        lse = torch.empty((B, H_Q, N), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H_Q, N) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 [B, H_Q, N] tensor")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        rc = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          lse.data_ptr() if lse is not None else None,
+                          B, H_Q, H_KV, N, d, int(bool(causal)),
+                          _mapping_id(mapping), _stream_handle(stream, q.device))
+    _check(rc, "attn_fwd")
+    return o, lse
+
+
+def attn_wg_map(mapping, B: int, H_Q: int, H_KV: int, N: int,
+                num_xcd: int) -> np.ndarray:
+    """The (b, h, m) of every workgroup id, int32 [W, 3] (host, no GPU)."""
+    W = num_workgroups(B, H_Q, N)
+    out = np.empty((max(W, 1), 3), dtype=np.int32)
+    rc = load_library().attn_wg_map(_mapping_id(mapping), B, H_Q, H_KV, N,
+                                    num_xcd, out.ctypes.data)
+    _check(rc, "attn_wg_map")
+    return out[:W]
+
+
+def attn_num_xcd() -> int:
+    rc = load_library().attn_num_xcd()
+    if rc < 0:
+        raise AttnError(rc, "attn_num_xcd")
+    return rc
+
+
+def attn_probe_placement(mapping, B: int, H_Q: int, H_KV: int, N: int,
+                         out: torch.Tensor | None = None, device="cuda",
+                         stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """int32 [W, 4] on the GPU: (xcc_id, b, h, m) per workgroup id."""
+    W = num_workgroups(B, H_Q, N)
+    if out is None:
+        out = torch.empty((W, 4), dtype=torch.int32, device=device)
+    lib = load_library()
+    with torch.cuda.device(out.device):
+        rc = lib.attn_probe_placement(_mapping_id(mapping), B, H_Q, H_KV, N,
+                                      out.data_ptr(),
+                                      _stream_handle(stream, out.device))
+    _check(rc, "attn_probe_placement")
+    return out

@@ -1,0 +1,54 @@
+"""Builds libattn_numa.so (the HIP kernels and the C ABI) in-tree for gfx950.
+
+Usage: python -m chiplet_numa_aware_amd.build  (or build() from Python).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libattn_numa.so")
+SOURCES = [os.path.join(CSRC, "attn_numa.hip")]
+ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def command(out: str = LIB) -> list[str]:
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+        "-shared", "-fPIC",
+        # No packed-fp32 VALU instructions anywhere in the device code.
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", os.path.join(ROOT, "include"),
+        "-Wall", "-Wno-unused-function",
+        *SOURCES, "-o", out,
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles the library (always) and returns its path."""
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,228 @@
+// C ABI of the attention forward library (declared in include/attn_numa.h).
+//
+// Host side: argument validation, the per-device XCD count, choice of the
+// kernel instantiation (padded head dim 64/128 x causal) and the launch on
+// the caller's stream.  No entry point allocates or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+
+#include "../../include/attn_numa.h"
+#include "attn_fwd_kernel.hpp"
+#include "wg_map.hpp"
+
+namespace attn_numa {
+namespace {
+
+thread_local char g_err_text[256];
+
+int hip_fail(hipError_t e, const char* what) {
+  std::snprintf(g_err_text, sizeof(g_err_text), "HIP error in %s: %s (%d)",
+                what, hipGetErrorString(e), (int)e);
+  return ATTN_E_HIP;
+}
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// Validates the shape; on success stores the row-block count and grid size.
+int check_shape(int B, int H_Q, int H_KV, int N, int* M_out, int* W_out) {
+  if (B <= 0 || H_Q <= 0 || H_KV <= 0 || N <= 0) return ATTN_E_SHAPE;
+  if (H_Q % H_KV != 0) return ATTN_E_SHAPE;
+  const int64_t M = ((int64_t)N + kBlockM - 1) / kBlockM;
+  const int64_t W = (int64_t)B * H_Q * M;
+  if (W >= (int64_t(1) << 31)) return ATTN_E_SHAPE;
+  *M_out = (int)M;
+  *W_out = (int)W;
+  return ATTN_OK;
+}
+
+int check_head_dim(int N, int d) {
+  if (d <= 0 || d > 128 || (d % 8) != 0) return ATTN_E_HEAD_DIM;
+  // One head must fit a buffer resource (byte offsets are 32-bit signed).
+  if ((int64_t)N * d * 2 >= (int64_t(1) << 31)) return ATTN_E_SHAPE;
+  return ATTN_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_xcd_once[kMaxDevices];
+int g_xcd[kMaxDevices];
+
+int env_xcd_override() {
+  const char* s = std::getenv("ATTN_NUM_XCD");
+  if (!s || !*s) return 0;
+  char* end = nullptr;
+  long v = std::strtol(s, &end, 10);
+  if (end == s || *end != '\0' || v < 1 || v > 64) return 0;
+  return (int)v;
+}
+
+int device_xcd_count(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return ATTN_E_NO_DEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_E_NO_DEVICE;
+  std::call_once(g_xcd_once[dev], [dev]() {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) !=
+            hipSuccess ||
+        n < 1)
+      n = 1;
+    g_xcd[dev] = n;
+  });
+  *out = g_xcd[dev];
+  return ATTN_OK;
+}
+
+int resolve_xcd(int* out) {
+  int n = 0;
+  int devs = 0;
+  if (hipGetDeviceCount(&devs) != hipSuccess || devs <= 0)
+    return ATTN_E_NO_DEVICE;
+  const int over = env_xcd_override();
+  if (over > 0) {
+    *out = over;
+    return ATTN_OK;
+  }
+  int rc = device_xcd_count(&n);
+  if (rc != ATTN_OK) return rc;
+  *out = n;
+  return ATTN_OK;
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const void* q, const void* k, const void* v, void* o,
+                  float* lse, int B, int H_Q, int H_KV, int N, int d, int M,
+                  int W, int mapping, int X, float scale_log2,
+                  hipStream_t stream) {
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(W), dim3(kThreads), 0,
+                     stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
+                     lse, B, H_Q, H_KV, N, d, M, mapping, X, scale_log2);
+  return hipGetLastError();
+}
+
+// Placement probe: one wave per workgroup; lane 0 records the XCC id the
+// workgroup runs on and the coordinates the remap gives it.
+__global__ void probe_kernel(int32_t* out, int B, int H_Q, int M, int mapping,
+                             int X) {
+  if (threadIdx.x != 0) return;
+  uint32_t xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  const WgCoord c = wg_map(mapping, blockIdx.x, B, H_Q, M, X);
+  int32_t* p = out + 4 * (uint64_t)blockIdx.x;
+  p[0] = (int32_t)(xcc & 0xF);
+  p[1] = (int32_t)c.b;
+  p[2] = (int32_t)c.h;
+  p[3] = (int32_t)c.m;
+}
+
+}  // namespace
+}  // namespace attn_numa
+
+using namespace attn_numa;
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H_Q, int H_KV, int N, int d, int causal, int mapping,
+             void* stream) {
+  if (!q || !k || !v || !o) return ATTN_E_NULL;
+  int M = 0, W = 0;
+  int rc = check_shape(B, H_Q, H_KV, N, &M, &W);
+  if (rc != ATTN_OK) return rc;
+  rc = check_head_dim(N, d);
+  if (rc != ATTN_OK) return rc;
+  if (mapping < 0 || mapping > 3) return ATTN_E_MAPPING;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && !aligned16(lse)))
+    return ATTN_E_ALIGN;
+  int X = 1;
+  rc = resolve_xcd(&X);
+  if (rc != ATTN_OK) return rc;
+  const float scale_log2 =
+      (float)(1.4426950408889634 / std::sqrt((double)d));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (d <= 64) {
+    e = causal ? launch<64, true>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W,
+                                  mapping, X, scale_log2, s)
+               : launch<64, false>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W,
+                                   mapping, X, scale_log2, s);
+  } else {
+    e = causal ? launch<128, true>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W,
+                                   mapping, X, scale_log2, s)
+               : launch<128, false>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W,
+                                    mapping, X, scale_log2, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
+  return ATTN_OK;
+}
+
+int attn_wg_map(int mapping, int B, int H_Q, int H_KV, int N, int num_xcd,
+                int32_t* out_host) {
+  if (!out_host) return ATTN_E_NULL;
+  int M = 0, W = 0;
+  int rc = check_shape(B, H_Q, H_KV, N, &M, &W);
+  if (rc != ATTN_OK) return rc;
+  if (num_xcd < 1) return ATTN_E_SHAPE;
+  if (mapping < 0 || mapping > 3) return ATTN_E_MAPPING;
+  for (int w = 0; w < W; ++w) {
+    const WgCoord c = wg_map(mapping, (uint32_t)w, (uint32_t)B, (uint32_t)H_Q,
+                             (uint32_t)M, (uint32_t)num_xcd);
+    out_host[3 * (int64_t)w + 0] = (int32_t)c.b;
+    out_host[3 * (int64_t)w + 1] = (int32_t)c.h;
+    out_host[3 * (int64_t)w + 2] = (int32_t)c.m;
+  }
+  return ATTN_OK;
+}
+
+int attn_num_xcd(void) {
+  int X = 0;
+  int rc = resolve_xcd(&X);
+  return rc == ATTN_OK ? X : rc;
+}
+
+int attn_probe_placement(int mapping, int B, int H_Q, int H_KV, int N,
+                         int32_t* dev_out, void* stream) {
+  if (!dev_out) return ATTN_E_NULL;
+  int M = 0, W = 0;
+  int rc = check_shape(B, H_Q, H_KV, N, &M, &W);
+  if (rc != ATTN_OK) return rc;
+  if (mapping < 0 || mapping > 3) return ATTN_E_MAPPING;
+  if (!aligned16(dev_out)) return ATTN_E_ALIGN;
+  int X = 1;
+  rc = resolve_xcd(&X);
+  if (rc != ATTN_OK) return rc;
+  hipLaunchKernelGGL(probe_kernel, dim3(W), dim3(64), 0,
+                     static_cast<hipStream_t>(stream), dev_out, B, H_Q, M,
+                     mapping, X);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "attn_probe_placement launch");
+  return ATTN_OK;
+}
+
+const char* attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_NULL: return "a required pointer is NULL";
+    case ATTN_E_SHAPE:
+      return "bad shape (B, H_Q, H_KV, N must be > 0, H_Q % H_KV == 0, "
+             "B*H_Q*ceil(N/128) < 2^31, N*d*2 < 2^31, num_xcd >= 1)";
+    case ATTN_E_HEAD_DIM: return "unsupported head dim (need 8 <= d <= 128, d % 8 == 0)";
+    case ATTN_E_MAPPING: return "mapping must be 0..3";
+    case ATTN_E_ALIGN: return "device pointer not 16-byte aligned";
+    case ATTN_E_HIP:
+      return g_err_text[0] ? g_err_text : "HIP runtime error";
+    case ATTN_E_NO_DEVICE: return "no HIP device visible";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

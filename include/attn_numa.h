@@ -1,0 +1,130 @@
+/*
+ * attn_numa: NUMA-aware FlashAttention-2 style attention forward for MI355X
+ * (gfx950), C ABI.
+ *
+ * The operation is scaled dot-product attention, S = Q K^T, P = softmax(S /
+ * sqrt(d)), O = P V, per head ("Optimizing Attention on GPUs by Exploiting GPU
+ * Architectural NUMA Effects", digest page, §4 equation), computed by one
+ * workgroup per (batch, query head, 128-row block) that streams all of that
+ * head's K and V with an online softmax (same page, §3 Figure 4).  Which
+ * workgroup takes which row block is set by one of four workgroup-ID remaps
+ * (same page, §2 Q2, §3 Figure 10 and the before/after table, §7 Figures 3
+ * and 11).
+ *
+ * Conventions for every entry point:
+ *   - Return value: 0 on success, a negative ATTN_E* code otherwise; nothing
+ *     is launched when validation fails.  attn_strerror(code) describes it.
+ *   - No entry point allocates, frees or synchronises device memory.  The
+ *     caller owns every buffer.  Device work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the null stream) and the call returns once it is
+ *     enqueued.
+ *   - Thread-safe: the only shared state is a per-device cache of device
+ *     attributes filled on first use.
+ */
+#ifndef ATTN_NUMA_H
+#define ATTN_NUMA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Error codes. */
+#define ATTN_OK 0
+#define ATTN_E_NULL (-1)        /* a required pointer is NULL */
+#define ATTN_E_SHAPE (-2)       /* B, H_Q, H_KV or N <= 0, H_Q % H_KV != 0,
+                                   or a size beyond the 32-bit limits below */
+#define ATTN_E_HEAD_DIM (-3)    /* d <= 0, d > 128 or d % 8 != 0 */
+#define ATTN_E_MAPPING (-4)     /* mapping not in 0..3 */
+#define ATTN_E_ALIGN (-5)       /* a device pointer is not 16-byte aligned */
+#define ATTN_E_HIP (-6)         /* HIP runtime or launch error */
+#define ATTN_E_NO_DEVICE (-7)   /* no HIP device is visible */
+
+/* Workgroup remap modes (digest page §3 before/after table, §5). */
+#define ATTN_MAP_NAIVE_BLOCK_FIRST 0    /* id order, heads fastest */
+#define ATTN_MAP_NAIVE_HEAD_FIRST 1     /* id order, row blocks fastest */
+#define ATTN_MAP_SWIZZLED_BLOCK_FIRST 2 /* chiplet swizzle, heads fastest */
+#define ATTN_MAP_SWIZZLED_HEAD_FIRST 3  /* chiplet swizzle, blocks fastest:
+                                           one ACC per XCD at a time */
+
+/*
+ * attn_fwd: attention forward pass.
+ *
+ * Passage: digest page §4 equation (the result) and §3 Figure 4 (the
+ * row-block tiling: one workgroup per 128 query rows of a head, reading all
+ * of that head's K and V).
+ *
+ *   q    device, bf16 [B][H_Q][N][d], contiguous, read only
+ *   k    device, bf16 [B][H_KV][N][d], contiguous, read only
+ *   v    device, bf16 [B][H_KV][N][d], contiguous, read only
+ *   o    device, bf16 [B][H_Q][N][d], contiguous, written (every element)
+ *   lse  device, fp32 [B][H_Q][N], written, may be NULL: natural-log
+ *        logsumexp of the scaled (and masked) scores of each query row
+ *   B, H_Q, H_KV, N, d   shape; H_Q % H_KV == 0; query head h reads KV head
+ *        h / (H_Q / H_KV); 8 <= d <= 128 with d % 8 == 0 (d <= 64 runs a
+ *        64-wide tile, else a 128-wide one); B*H_Q*ceil(N/128) < 2^31 and
+ *        N*d*2 < 2^31 bytes per head
+ *   causal  0: every key; 1: query row i sees keys 0..i (top-left aligned)
+ *   mapping ATTN_MAP_* (0..3); the XCD count used is attn_num_xcd()
+ *   stream  hipStream_t or NULL
+ *
+ * Arithmetic: bf16 inputs, fp32 scores, softmax statistics and accumulators;
+ * P is rounded to bf16 (nearest-even) before P V; O is rounded to bf16.
+ * O and lse do not depend on `mapping` (bit-identical across modes).
+ * Errors: ATTN_E_NULL (q, k, v or o NULL), ATTN_E_SHAPE, ATTN_E_HEAD_DIM,
+ * ATTN_E_MAPPING, ATTN_E_ALIGN (q, k, v, o or lse), ATTN_E_NO_DEVICE,
+ * ATTN_E_HIP (launch failed; attn_strerror(ATTN_E_HIP) has the HIP text).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H_Q, int H_KV, int N, int d, int causal, int mapping,
+             void* stream);
+
+/*
+ * attn_wg_map: the remap table the kernel uses, computed on the host.
+ *
+ * Passage: digest page §2 Q1 (dispatch to XCD w mod X), §2 Q2 and §7
+ * Figures 3 and 11 (the swizzles), §3 Figure 10.
+ *
+ *   out_host  host, int32 [W][3], W = B*H_Q*ceil(N/128); row w receives the
+ *             (batch, query head, row block) that workgroup w computes when
+ *             the chip has num_xcd XCDs.  Caller-owned.
+ *   num_xcd   >= 1 (pass attn_num_xcd() for the device's value)
+ * H_KV is validated like attn_fwd (the ACC structure depends on it) but the
+ * table itself does not.  Needs no GPU.
+ * Errors: ATTN_E_NULL, ATTN_E_SHAPE (also num_xcd < 1), ATTN_E_MAPPING.
+ */
+int attn_wg_map(int mapping, int B, int H_Q, int H_KV, int N, int num_xcd,
+                int32_t* out_host);
+
+/*
+ * attn_num_xcd: XCDs of the current device (8 on MI355X in SPX mode), the
+ * count attn_fwd swizzles over.  The environment variable ATTN_NUM_XCD (an
+ * integer 1..64) overrides it.  Returns the count (>= 1) or a negative
+ * ATTN_E_* code (ATTN_E_NO_DEVICE without a GPU).
+ */
+int attn_num_xcd(void);
+
+/*
+ * attn_probe_placement: where the hardware ran each workgroup.
+ *
+ * Launches the attention grid for this shape and mapping with a kernel that
+ * does no attention: workgroup w writes, at dev_out[4*w .. 4*w+3], the XCC
+ * id register it ran on and the (batch, query head, row block) the remap
+ * gives it.  Checks the dispatch model of digest page §2 Q1 on the device.
+ *
+ *   dev_out  device, int32 [W][4], W as in attn_wg_map, caller-owned.
+ * Errors: as attn_fwd (ATTN_E_NULL for dev_out).
+ */
+int attn_probe_placement(int mapping, int B, int H_Q, int H_KV, int N,
+                         int32_t* dev_out, void* stream);
+
+/* Text for an ATTN_E_* code; for ATTN_E_HIP, the calling thread's last HIP
+   error.  The pointer stays valid until the next call on the same thread. */
+const char* attn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_NUMA_H */

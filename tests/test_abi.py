@@ -1,0 +1,136 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, rejects bad arguments before touching a device, and its host
+remap table equals the independent oracle's."""
+import ctypes
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import chiplet_numa_aware_amd as attn
+import oracle
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "attn_numa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return attn.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def _declared_codes():
+    return {m.group(1): int(m.group(2)) for m in re.finditer(
+        r"#define\s+(ATTN_E_\w+|ATTN_OK)\s+\(?(-?\d+)\)?", open(HEADER).read())}
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == {"attn_fwd", "attn_wg_map", "attn_num_xcd",
+                          "attn_probe_placement", "attn_strerror"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_covers_every_code(lib):
+    codes = _declared_codes()
+    assert codes["ATTN_OK"] == 0
+    texts = set()
+    for name, c in codes.items():
+        t = attn.attn_strerror(c)
+        assert t and t != "unknown error code", name
+        texts.add(t)
+    assert len(texts) == len(codes)
+    assert attn.attn_strerror(12345) == "unknown error code"
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, H_Q=8, H_KV=8,
+         N=1024, d=128, causal=0, mapping=3):
+    return lib.attn_fwd(q, k, v, o, lse, B, H_Q, H_KV, N, d, causal, mapping, None)
+
+
+def test_fwd_argument_errors(lib):
+    c = _declared_codes()
+    for kw in ({"q": None}, {"k": None}, {"v": None}, {"o": None}):
+        assert _fwd(lib, **kw) == c["ATTN_E_NULL"]
+    for kw in ({"B": 0}, {"H_Q": 0}, {"H_KV": 0}, {"N": 0}, {"N": -5},
+               {"H_Q": 12, "H_KV": 8}, {"B": 1 << 20, "H_Q": 1024, "N": 1 << 20}):
+        assert _fwd(lib, **kw) == c["ATTN_E_SHAPE"], kw
+    for d in (0, -8, 4, 12, 136, 256):
+        assert _fwd(lib, d=d) == c["ATTN_E_HEAD_DIM"], d
+    # one head larger than 2 GiB does not fit a buffer resource
+    assert _fwd(lib, N=1 << 23, d=128, H_Q=1, H_KV=1) == c["ATTN_E_SHAPE"]
+    for m in (-1, 4, 99):
+        assert _fwd(lib, mapping=m) == c["ATTN_E_MAPPING"]
+    for kw in ({"q": FAKE + 2}, {"k": FAKE + 8}, {"v": FAKE + 1},
+               {"o": FAKE + 4}, {"lse": FAKE + 4}):
+        assert _fwd(lib, **kw) == c["ATTN_E_ALIGN"], kw
+
+
+def test_wg_map_and_probe_argument_errors(lib):
+    c = _declared_codes()
+    buf = np.zeros(64 * 3, dtype=np.int32)
+    assert lib.attn_wg_map(3, 1, 8, 8, 1024, 8, None) == c["ATTN_E_NULL"]
+    assert lib.attn_wg_map(3, 1, 8, 3, 1024, 8, buf.ctypes.data) == c["ATTN_E_SHAPE"]
+    assert lib.attn_wg_map(3, 1, 8, 8, 1024, 0, buf.ctypes.data) == c["ATTN_E_SHAPE"]
+    assert lib.attn_wg_map(4, 1, 8, 8, 1024, 8, buf.ctypes.data) == c["ATTN_E_MAPPING"]
+    assert lib.attn_probe_placement(3, 1, 8, 8, 1024, None, None) == c["ATTN_E_NULL"]
+    assert lib.attn_probe_placement(3, 0, 8, 8, 1024, FAKE, None) == c["ATTN_E_SHAPE"]
+    assert lib.attn_probe_placement(7, 1, 8, 8, 1024, FAKE, None) == c["ATTN_E_MAPPING"]
+    assert lib.attn_probe_placement(3, 1, 8, 8, 1024, FAKE + 4, None) == c["ATTN_E_ALIGN"]
+
+
+def _shapes():
+    shapes = [(1, 8, 8, 1024, 8), (1, 128, 128, 8192, 8), (1, 64, 8, 131072, 8),
+              (2, 32, 4, 32768, 8), (2, 12, 12, 32768, 8), (1, 12, 12, 32768, 8),
+              (1, 128, 128, 131072, 8), (1, 8, 8, 128 * 128, 4)]
+    rng = random.Random(3)
+    for _ in range(150):
+        H_KV = rng.randint(1, 9)
+        H_Q = H_KV * rng.randint(1, 4)
+        shapes.append((rng.randint(1, 4), H_Q, H_KV, rng.randint(1, 2600),
+                       rng.choice([1, 2, 3, 4, 6, 8, 16])))
+    return shapes
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+def test_host_wg_map_equals_oracle(mode):
+    for B, H_Q, H_KV, N, X in _shapes():
+        got = attn.attn_wg_map(mode, B, H_Q, H_KV, N, X)
+        W = oracle.num_workgroups(B, H_Q, N)
+        assert got.shape == (W, 3)
+        if W > 20000:  # spot-check the large tables
+            idx = np.random.default_rng(W).integers(0, W, 4000)
+        else:
+            idx = np.arange(W)
+        exp = np.array([oracle.wg_map(mode, int(w), B, H_Q, N, X) for w in idx],
+                       dtype=np.int32).reshape(-1, 3)
+        assert np.array_equal(got[idx], exp), (mode, B, H_Q, H_KV, N, X)
+
+
+def test_host_wg_map_is_bijection_on_headline_shape():
+    for mode in range(4):
+        t = attn.attn_wg_map(mode, 1, 128, 128, 131072, 8).astype(np.int64)
+        key = (t[:, 0] * 128 + t[:, 1]) * 1024 + t[:, 2]
+        assert np.unique(key).size == t.shape[0] == 131072
+
+
+def test_num_xcd_env_override(monkeypatch):
+    """ATTN_NUM_XCD is read on every call; without a GPU the call reports
+    that no device is visible."""
+    lib = attn.load_library()
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("covered by the GPU placement test")
+    assert lib.attn_num_xcd() == _declared_codes()["ATTN_E_NO_DEVICE"]
