@@ -49,6 +49,8 @@ WORKLOADS = {
     "dsv3_d56_128k_causal": (1, 128, 128, 131072, 56, True),
     "dsv3_d56_32k_causal": (1, 128, 128, 32768, 56, True),
     "mha_h8_1k": (1, 8, 8, 1024, 128, False),
+    # K/V of one head (2 MiB) fits an XCD's L2: the kernel's compute-bound rate.
+    "mha_b16_4k": (16, 128, 128, 4096, 128, False),
 }
 
 
@@ -173,6 +175,9 @@ def main():
                          "3 (or the last one) is the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (twice), the "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -189,6 +194,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}))
+        return
     attn.load_library()
     B, H_Q, H_KV, N, d, causal = WORKLOADS[args.workload]
     modes = [int(m) for m in args.modes.split(",") if m.strip() != ""]

@@ -6,7 +6,7 @@
 // Figure 4 and the §4 equation).  Which block a workgroup takes comes from
 // wg_map.hpp.
 //
-// Layout of the work inside a workgroup (256 threads = 4 waves of 64):
+// Work inside a workgroup (256 threads = 4 waves of 64):
 //   * wave w owns query rows [32w, 32w+32) of the block; lane l owns query
 //     row 32w + (l mod 32); lanes l and l^32 share a row and split its keys.
 //   * scores are computed transposed, S^T = K Q^T, with
@@ -15,18 +15,30 @@
 //     accumulators of a 32x32 block are 16 keys of ITS query row: the row max
 //     and row sum are in-lane plus one exchange with lane l^32.
 //   * O^T = V^T P^T: P stays in the registers the score MFMA wrote (B operand,
-//     16 keys x 32 queries); V^T comes from LDS, where each tile of V is stored
-//     transposed ([dim][key]) with keys permuted inside every 16-key chunk so
-//     that the 8 keys a lane needs are 16 contiguous bytes.
-//   * K and V tiles (BLOCK_N keys) are double-buffered in LDS; tile j+1 is
-//     fetched from global memory into registers while tile j is computed.
-//   * m (row max, log2 units) and l (row sum) and O live in registers for the
-//     whole key loop; O is divided by l once at the end.
+//     16 keys x 32 queries); the V^T operand is read from V's row-major LDS
+//     tile with the gfx950 transposing LDS read (ds_read_b64_tr_b16).
+//   * K and V tiles go from global memory straight into LDS (buffer loads
+//     with the LDS-direct bit, no staging registers).  A tile is 64 rows of
+//     D/8 16-byte chunks; chunk c of row r sits at slot c ^ (r & 7), which
+//     keeps both the K operand reads and the transposing V reads free of
+//     bank conflicts.
+//   * software pipeline, one barrier per key tile j: the score MFMAs of tile
+//     j+1 are issued before the softmax of tile j so the matrix cores work
+//     while the VALU exponentiates; K runs one tile ahead of V in LDS (two K
+//     and two V buffers), and each tile's loads are issued one iteration
+//     before it is read.
+//   * online softmax in log2 units with the scale folded into one FMA; the
+//     running max m is raised (and O, l rescaled) only when a tile's max
+//     exceeds it by more than 2^8, so P <= 256: O / l is unchanged and bf16
+//     keeps its relative precision at any scale.
+//   * m, l and O live in registers for the whole key loop; O is divided by l
+//     once at the end.
 //
 // Global memory is read and written through buffer resources that cover one
 // head (at most 2^31 bytes): rows past N read as zero and stores past N are
-// dropped, which handles ragged N without branches and keeps all 64-bit
-// address arithmetic scalar.
+// dropped, so ragged N needs no branches; padded head-dim columns use an
+// offset that is always out of range.  All 64-bit address arithmetic is
+// scalar.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -44,6 +56,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBlockN = 64;     // keys per K/V tile
 constexpr int kThreads = 256;   // 4 waves
 constexpr uint32_t kBufDword3 = 0x00020000u;  // raw buffer, 32-bit data
+constexpr uint32_t kOutOfRange = 0x80000000u; // >= any head's byte size
+constexpr float kRescaleSlack = 8.0f;         // log2 of the largest P
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
                                                           uint32_t bytes) {
@@ -51,8 +65,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
                                            (int)bytes, (int)kBufDword3);
 }
 
-// Two bf16 lanes of two dwords packed into one dword: lo16 from a, lo16 from
-// b (sel = 0) or hi16 from a, hi16 from b (sel = 1).
+// Raw buffer descriptor (four SGPRs) for LDS-direct loads written as inline
+// assembly: base address, stride 0, size in bytes, 32-bit data format.
+__device__ __forceinline__ u32x4 make_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, kBufDword3};
+}
+
+// 16 bytes per lane from buffer `desc` at byte offset `voff` into LDS at
+// lds_byte + 16 * lane (out-of-range lanes write nothing).  Issued as inline
+// assembly so that the compiler does not treat every later LDS read as
+// depending on it; the caller waits (s_waitcnt vmcnt) before a barrier.
+__device__ __forceinline__ void load_lds_b128(u32x4 desc, uint32_t voff,
+                                              uint32_t lds_byte) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_byte), "v"(voff), "s"(desc)
+      : "memory", "m0");
+}
+
+// lo16(a) | lo16(b) << 16 and hi16(a) | hi16(b) << 16.
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
@@ -87,64 +121,79 @@ struct TileCfg {
   static constexpr int DB = D / 32;                // 32-dim blocks of O^T
   static constexpr int NB = kBlockN / 32;          // 32-key blocks of S^T
   static constexpr int NC = kBlockN / 16;          // 16-key chunks (PV k)
-  // LDS row strides in dwords.  stride = 4 (mod 32) makes the 8 lanes of a
-  // 16-byte LDS access with consecutive rows hit 8 disjoint bank quads.
-  static constexpr int KS = D / 2 + 4;             // K: [key][dim]
-  static constexpr int VS = kBlockN / 2 + 4;       // V^T: [dim][key slot]
-  static constexpr int K_DW = kBlockN * KS;
-  static constexpr int V_DW = D * VS;
-  static constexpr int STAGE_DW = K_DW + V_DW;
-  static constexpr int LDS_BYTES = 2 * STAGE_DW * 4;
-  // K: 16-byte chunks per thread per tile.
-  static constexpr int K_CHUNKS_PER_ROW = D / 8;
-  static constexpr int K_LOADS = kBlockN * K_CHUNKS_PER_ROW / kThreads;
-  // V: each thread loads VEC consecutive dims of 8 keys (keys
-  // 16c + 8h + 4g + j, h in {0,1}, j in 0..3), which land in 8 consecutive
-  // key slots 16c + 8g .. 16c + 8g + 7 of V^T.
-  static constexpr int VEC = D / 32;               // 4 (D=128) or 2 (D=64)
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;               // bytes per LDS row
+  static constexpr int TILE_B = kBlockN * ROWB;    // bytes per K or V tile
+  static constexpr int LDS_B = 4 * TILE_B;         // 2 K + 2 V buffers
+  // 16-byte LDS-direct loads per thread per operand and tile; one wave
+  // instruction fills 64 consecutive 16-byte slots (1 KiB).
+  static constexpr int LOADS = kBlockN * CPR / kThreads;
 };
 
-// Key slot of key offset o (0..15) inside its 16-key chunk: swaps bits 2 and
-// 3, so that the keys a PV MFMA lane holds (o = 8h + 4g + j) sit at
-// 8g + 4h + j.
+// Static schedule of one steady key tile for one wave.
 //
-// V^T thread mapping (t = thread id): for each tile, thread t handles
-//   g = lane bit 0, and dims/chunks chosen so that the 8 lanes of an LDS
-//   quarter-wave write 8 disjoint bank quads (stride VS = 4 mod 32):
-//   D=128 (VEC 4): lane bits [g, dv0, c0], D=64 (VEC 2): lane bits [g, dv0, dv1].
+// The tile issues T = NS + NP MFMAs (NS score MFMAs of the next tile, then NP
+// P V MFMAs of this tile).  Each MFMA is a "bundle": it also issues the LDS
+// read of the MFMA operand kDist bundles ahead and a slice of the tile's VALU
+// work, so the VALU runs in the MFMA shadow and LDS latency is covered.  The
+// VALU work is a list of steps, in dependency order:
+//   chunk c = 0..NC-1: 8 x (fma + exp2) of P, 4 x pack to bf16, 4 x two adds
+//                      of the row sum  (the packs precede chunk c's P V MFMAs)
+//   max of the next tile's scores: NB*8 x max3  (after its score MFMAs)
+// and is spread over the bundles in proportion to its cost (4-cycle units;
+// fma + exp2 counts 3).
 template <int D>
-struct VMap {
-  int g, c, dv;
-  __device__ __forceinline__ explicit VMap(int t) {
-    const int lane = t & 63, wave = t >> 6;
-    g = lane & 1;
-    if (D == 128) {
-      // 32 dim groups of 4 (dv) x 4 chunks (c): wave w covers dv in [8w, 8w+8)
-      const int dv0 = (lane >> 1) & 1, c0 = (lane >> 2) & 1;
-      const int c1 = (lane >> 3) & 1, dvh = (lane >> 4) & 3;
-      c = c0 | (c1 << 1);
-      dv = wave * 8 + (dv0 | (dvh << 1));
-    } else {
-      // 32 dim groups of 2 (dv) x 4 chunks (c): wave w covers dv in [8w, 8w+8)
-      const int dvl = (lane >> 1) & 3, c01 = (lane >> 3) & 3, dvh = (lane >> 5) & 1;
-      c = c01;
-      dv = wave * 8 + (dvl | (dvh << 2));
-    }
+struct TileSchedule {
+  using C = TileCfg<D>;
+  static constexpr int NS = C::NB * C::KC;
+  static constexpr int NP = C::NC * C::DB;
+  static constexpr int T = NS + NP;
+  static constexpr int STEPS_PER_CHUNK = 16;
+  static constexpr int EXP_STEPS = C::NC * STEPS_PER_CHUNK;
+  static constexpr int MAX_STEPS = C::NB * 8;
+  static constexpr int STEPS = EXP_STEPS + MAX_STEPS;
+  static constexpr int cost(int s) {
+    if (s >= EXP_STEPS) return 1;
+    const int k = s % STEPS_PER_CHUNK;
+    return k < 8 ? 3 : (k < 12 ? 1 : 2);
+  }
+  static constexpr int total_cost() {
+    int c = 0;
+    for (int s = 0; s < STEPS; ++s) c += cost(s);
+    return c;
+  }
+  // Bundle that runs step s: the one whose share of the total cost contains
+  // the step's starting cost.
+  static constexpr int bundle(int s) {
+    int c = 0;
+    for (int i = 0; i < s; ++i) c += cost(i);
+    return c * T / total_cost();
+  }
+  // Score MFMAs of the next tile finish within the first NS bundles; the max
+  // steps must come after them, and the bf16 packs of chunk c (its steps
+  // 8..11) before P V MFMA NS + c*DB, which opens bundle NS + c*DB.
+  static constexpr bool valid() {
+    for (int ch = 0; ch < C::NC; ++ch)
+      if (bundle(ch * STEPS_PER_CHUNK + 11) >= NS + ch * C::DB) return false;
+    return bundle(EXP_STEPS) >= NS;
   }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool FULL_D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, int B, int H_Q, int H_KV, int N, int d, int M,
     int mapping, int num_xcd, float scale_log2) {
   using C = TileCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint32_t lds[2 * C::STAGE_DW];
+  __shared__ __attribute__((aligned(16))) uint32_t lds[C::LDS_B / 4];
+  char* const lds_b = reinterpret_cast<char*>(lds);
+  // K buffers at [0, 2*TILE_B), V buffers at [2*TILE_B, 4*TILE_B).
+  constexpr int kVBase = 2 * C::TILE_B;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int g = lane >> 5;     // lane half: which 8 of 16 MFMA k values
   const int l32 = lane & 31;   // query row within the wave / MFMA column
 
@@ -152,13 +201,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int kvh = (int)wc.h / (H_Q / H_KV);
   const int row0 = (int)wc.m * kBlockM;
 
-  const uint32_t head_elems = (uint32_t)N * (uint32_t)d;
+  // Row length in elements: the compile-time D when d == D, so that every
+  // per-lane offset below is a constant multiple and folds into immediates.
+  const int dd = FULL_D ? D : d;
+  const uint32_t head_elems = (uint32_t)N * (uint32_t)dd;
   const uint64_t q_head = ((uint64_t)wc.b * H_Q + wc.h) * head_elems;
   const uint64_t kv_head = ((uint64_t)wc.b * H_KV + kvh) * head_elems;
   const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(q + q_head, head_elems * 2);
-  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + kv_head, head_elems * 2);
-  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v + kv_head, head_elems * 2);
   const __amdgpu_buffer_rsrc_t o_rs = make_rsrc(o + q_head, head_elems * 2);
+  const u32x4 k_desc = make_desc(k + kv_head, head_elems * 2);
+  const u32x4 v_desc = make_desc(v + kv_head, head_elems * 2);
 
   // ---- Q fragments: B operand of S^T = K Q^T, lane holds Q[row][16kc+8g..+7].
   const int my_row = row0 + wave * 32 + l32;
@@ -166,195 +218,296 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
   for (int kc = 0; kc < C::KC; ++kc) {
     const int col = kc * 16 + g * 8;
-    u32x4 t = {0u, 0u, 0u, 0u};
-    if (col < d)
-      t = __builtin_amdgcn_raw_buffer_load_b128(
-          q_rs, (my_row * d + col) * 2, 0, 0);
-    qf[kc] = __builtin_bit_cast(bf16x8, t);
+    const uint32_t off = (FULL_D || col < dd)
+                             ? (uint32_t)(my_row * dd + col) * 2u
+                             : kOutOfRange;
+    qf[kc] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(q_rs, off, 0, 0));
   }
 
-  // ---- tile count
-  const int n_tiles_all = (N + kBlockN - 1) / kBlockN;
-  int n_tiles = n_tiles_all;
-  if (CAUSAL) {
-    const int last = (row0 + kBlockM + kBlockN - 1) / kBlockN;
-    n_tiles = last < n_tiles_all ? last : n_tiles_all;
+  // ---- LDS-direct tile loads.  Wave instruction i of wave w fills the 1 KiB
+  // block i*4 + w of the tile: lane l writes slot P = 64*(i*4+w) + l, i.e.
+  // row P / CPR, slot P % CPR, which holds the row's chunk (slot ^ (row & 7)).
+  // Chunks past the head dim get an out-of-range offset and are never
+  // written (the buffer was zeroed); rows past N read zero.
+  uint32_t ld_off[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int P = (i * 4 + wave) * 64 + lane;
+    const int row = P / C::CPR;
+    const int chunk = (P % C::CPR) ^ (row & 7);
+    ld_off[i] = (FULL_D || chunk * 8 < dd) ? (uint32_t)(row * dd + chunk * 8) * 2u
+                                           : kOutOfRange;
   }
-
-  // ---- global -> register staging for one K/V tile
-  u32x4 kreg[C::K_LOADS];
-  uint32_t vreg[8][C::VEC / 2];
-  const VMap<D> vm(tid);
-
-  auto load_tile = [&](int tile) {
-    const int key0 = tile * kBlockN;
+  const uint32_t tile_bytes = (uint32_t)kBlockN * (uint32_t)dd * 2u;
+  // An out-of-range offset stays out of range after adding a tile base (both
+  // are below 2^31).
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(
+      (__attribute__((address_space(3))) char*)lds_b);
+  auto load_tile = [&](u32x4 desc, int tile, int lds_byte) {
+    const uint32_t base = (uint32_t)tile * tile_bytes;
 #pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
-      const int chunk = tid + i * kThreads;
-      const int r = chunk / C::K_CHUNKS_PER_ROW;
-      const int col = (chunk % C::K_CHUNKS_PER_ROW) * 8;
-      u32x4 t = {0u, 0u, 0u, 0u};
-      if (col < d)
-        t = __builtin_amdgcn_raw_buffer_load_b128(
-            k_rs, ((key0 + r) * d + col) * 2, 0, 0);
-      kreg[i] = t;
-    }
-    const int col = vm.dv * C::VEC;
+    for (int i = 0; i < C::LOADS; ++i)
+      load_lds_b128(desc, ld_off[i] + base,
+                    lds_base + lds_byte + (i * 4 + wave) * 1024);
+  };
+  auto load_k = [&](int tile, int buf) { load_tile(k_desc, tile, buf * C::TILE_B); };
+  auto load_v = [&](int tile, int buf) { load_tile(v_desc, tile, kVBase + buf * C::TILE_B); };
+  // All of this wave's LDS-direct loads have landed (then a barrier makes
+  // every wave's visible).
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0); };
+
+  // ---- LDS operand addresses (bytes).  K: row nb*32 + l32, chunk 2kc + g.
+  int k_addr[C::KC];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int h = e >> 2, j = e & 3;
-      const int key = key0 + vm.c * 16 + h * 8 + vm.g * 4 + j;
-      const int off = (key * d + col) * 2;
-      if constexpr (C::VEC == 4) {
-        u32x2 t = {0u, 0u};
-        if (col < d) t = __builtin_amdgcn_raw_buffer_load_b64(v_rs, off, 0, 0);
-        vreg[e][0] = t.x;
-        vreg[e][1] = t.y;
-      } else {
-        uint32_t t = 0u;
-        if (col < d) t = __builtin_amdgcn_raw_buffer_load_b32(v_rs, off, 0, 0);
-        vreg[e][0] = t;
-      }
-    }
+  for (int kc = 0; kc < C::KC; ++kc)
+    k_addr[kc] = l32 * C::ROWB + (((kc * 2 + g) ^ (l32 & 7)) * 16);
+  // V^T through ds_read_b64_tr_b16: in each 16-lane group, source lane
+  // 4k + q addresses key 16c + 8h + 4g + k, dims 32db + 16*dhalf + 4q..+3,
+  // and output lane j receives dim 32db + 16*dhalf + j of the 4 keys.
+  int v_addr[C::DB];
+  {
+    const int j = lane & 15, kk = j >> 2, qq = j & 3;
+    const int dhalf = (lane >> 4) & 1;
+    const int krow = 4 * g + kk;                 // key & 7 of the 4 keys
+    const int w = 2 * dhalf + (qq >> 1);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+      v_addr[db] = kVBase + krow * C::ROWB + (((4 * db + w) ^ krow) * 16) + (qq & 1) * 8;
+  }
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  auto k_operand = [&](int buf, int nb, int kc) {
+    return *reinterpret_cast<const bf16x8*>(lds_b + buf * C::TILE_B + k_addr[kc] +
+                                            nb * 32 * C::ROWB);
+  };
+  auto v_operand = [&](int buf, int c, int db) {
+    const char* p = lds_b + buf * C::TILE_B + v_addr[db] + c * 16 * C::ROWB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p + 8 * C::ROWB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  auto store_tile = [&](int stage) {
-    uint32_t* ks = lds + stage * C::STAGE_DW;
-    uint32_t* vs = ks + C::K_DW;
+  // S^T = K Q^T for one tile from K buffer `buf`: s[nb] = keys 32nb..32nb+31.
+  auto scores = [&](int buf, f32x16* s) {
 #pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
-      const int chunk = tid + i * kThreads;
-      const int r = chunk / C::K_CHUNKS_PER_ROW;
-      const int cc = chunk % C::K_CHUNKS_PER_ROW;
-      *reinterpret_cast<u32x4*>(ks + r * C::KS + cc * 4) = kreg[i];
-    }
-    // V^T: for each of my VEC dims, 8 keys -> 16 bytes at slot 16c + 8g.
+    for (int nb = 0; nb < C::NB; ++nb) {
+      f32x16 acc = {};
 #pragma unroll
-    for (int jj = 0; jj < C::VEC; ++jj) {
-      const int w = jj >> 1;
-      u32x4 t;
-      if ((jj & 1) == 0) {
-        t.x = pack_lo(vreg[0][w], vreg[1][w]);
-        t.y = pack_lo(vreg[2][w], vreg[3][w]);
-        t.z = pack_lo(vreg[4][w], vreg[5][w]);
-        t.w = pack_lo(vreg[6][w], vreg[7][w]);
-      } else {
-        t.x = pack_hi(vreg[0][w], vreg[1][w]);
-        t.y = pack_hi(vreg[2][w], vreg[3][w]);
-        t.z = pack_hi(vreg[4][w], vreg[5][w]);
-        t.w = pack_hi(vreg[6][w], vreg[7][w]);
-      }
-      const int dim = vm.dv * C::VEC + jj;
-      *reinterpret_cast<u32x4*>(vs + dim * C::VS + vm.c * 8 + vm.g * 4) = t;
+      for (int kc = 0; kc < C::KC; ++kc)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(buf, nb, kc),
+                                                      qf[kc], acc, 0, 0, 0);
+      s[nb] = acc;
     }
   };
 
   // ---- running state
   f32x16 oacc[C::DB];
 #pragma unroll
-  for (int i = 0; i < C::DB; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-  float m_run = -INFINITY;  // running max of scaled scores, log2 units
+  for (int i = 0; i < C::DB; ++i) oacc[i] = f32x16{};
+  float m_run = -INFINITY;  // running max of scaled scores, log2 units (lazy)
   float l_run = 0.f;        // this lane's share of the running row sum
 
-  const int wave_row_last = row0 + wave * 32 + 31;
+  // Scaled row max of a tile of scores (log2 units), both lane halves.
+  auto tile_max = [&](const f32x16* s) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
+    return xhalf_max(mx) * scale_log2;
+  };
 
-  load_tile(0);
-  store_tile(0);
+  // Raise m only when a tile's max exceeds it by more than the slack (always
+  // on the first tile, where m = -inf); the decision is per wave.  Returns the
+  // offset to subtract before exponentiating.
+  auto update_max = [&](float mx) {
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      // A lane with no visible key yet keeps alpha = 1 (no -inf - -inf).
+      const float alpha =
+          (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int i = 0; i < C::DB; ++i) oacc[i] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    return (m_run == -INFINITY) ? 0.f : m_run;
+  };
+
+  // P = exp2(S * scale - m), l += sum of P in fp32 (before rounding, so that
+  // lse is the logsumexp of the scores to fp32 accuracy), P rounded to bf16,
+  // and O^T += V^T P^T from V buffer `buf`, one 16-key chunk at a time.
+  auto exp_pv = [&](const f32x16* s, float m_use, int buf) {
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+      const int nb = c >> 1, r0 = (c & 1) * 8;
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        p[e] = __builtin_amdgcn_exp2f(
+            __builtin_fmaf(s[nb][r0 + e], scale_log2, -m_use));
+      // The packed words stay scalars until the MFMA operand is formed: a
+      // bit-cast of one element of a 4 x u32 vector to bf16x2 has been
+      // miscompiled (to element 0) by this compiler.
+      uint32_t pk[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pk[w] = pack_bf16x2(p[2 * w], p[2 * w + 1]);
+        l_run += p[2 * w] + p[2 * w + 1];
+      }
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(buf, c, db),
+                                                           pb, oacc[db], 0, 0, 0);
+    }
+  };
+
+  // Mask keys past N and (causal) keys after the query row; accumulator r of
+  // block nb is key key0 + 32nb + 8(r/4) + 4g + (r%4).
+  auto mask = [&](f32x16* s, int key0) {
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + nb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+        const bool ok = key < N && (!CAUSAL || key <= my_row);
+        s[nb][r] = ok ? s[nb][r] : -INFINITY;
+      }
+  };
+
+  // ---- tiles
+  const int n_tiles_all = (N + kBlockN - 1) / kBlockN;
+  int n_tiles = n_tiles_all;
+  if (CAUSAL) {
+    const int last = (row0 + kBlockM + kBlockN - 1) / kBlockN;
+    n_tiles = last < n_tiles_all ? last : n_tiles_all;
+  }
+  // Steady tiles need no mask for any row of the workgroup and have a
+  // successor: keys of tile j all < N and (causal) <= the block's first row.
+  int n_steady = N / kBlockN;
+  if (CAUSAL) {
+    const int full = (row0 + 1) / kBlockN;
+    n_steady = full < n_steady ? full : n_steady;
+  }
+  if (n_steady > n_tiles - 1) n_steady = n_tiles - 1;
+  const int wave_row_first = row0 + wave * 32;
+  const int wave_row_last = wave_row_first + 31;
+
+  // ---- prologue: zero LDS (slots no load writes must read as zero), then
+  // K0, V0 -> buffers 0, K1 -> K buffer 1; S_0.
+#pragma unroll
+  for (int i = 0; i < C::LDS_B / 16 / kThreads; ++i)
+    *reinterpret_cast<u32x4*>(lds_b + (i * kThreads + tid) * 16) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  load_k(0, 0);
+  load_v(0, 0);
+  if (n_tiles > 1) load_k(1, 1);
+  wait_loads();
+  __syncthreads();
+  f32x16 s_cur[C::NB], s_next[C::NB];
+  scores(0, s_cur);
   __syncthreads();
 
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int stage = tile & 1;
-    const bool has_next = tile + 1 < n_tiles;
-    if (has_next) load_tile(tile + 1);
-
-    const int key0 = tile * kBlockN;
-    // Causal: a wave whose last row precedes this tile has nothing to do.
-    const bool active = !CAUSAL || key0 <= wave_row_last;
-    if (active) {
-      const uint32_t* ks = lds + stage * C::STAGE_DW;
-      const uint32_t* vs = ks + C::K_DW;
-
-      // S^T = K Q^T for the tile: sacc[nb] holds keys 32nb..32nb+31.
-      f32x16 sacc[C::NB];
+  int j = 0;
+  // Steady state: one basic block per tile after the (rare) rescale branch.
+  // Tile j+2's K (clamped to the last tile: a re-load that is never read) and
+  // tile j+1's V are fetched while S_{j+1} = K Q^T and the softmax and P V of
+  // tile j run; the row max of S_{j+1} is taken under the P V MFMAs.  The
+  // schedule interleaves each MFMA with the VALU work of the other stage.
+  float mx_cur = tile_max(s_cur);  // used only while tiles are steady
+  using TS = TileSchedule<D>;
+  static_assert(TS::valid(), "tile schedule breaks a data dependency");
+  constexpr int kDist = 3;  // LDS operand prefetch distance, in MFMAs
+  for (; j < n_steady; ++j) {
+    const float m_use = update_max(mx_cur);
+    // LDS operand of MFMA t: a K fragment (score MFMAs) or a V^T fragment.
+    auto operand = [&](int t) {
+      if (t < TS::NS) return k_operand((j + 1) & 1, t / C::KC, t % C::KC);
+      const int u = t - TS::NS;
+      return v_operand(j & 1, u / C::DB, u % C::DB);
+    };
+    // K of tile j+2 (clamped to the last tile: a re-load that is never read)
+    // and V of tile j+1 go to the buffers this iteration does not read.
+    load_k((j + 2 < n_tiles) ? j + 2 : n_tiles - 1, j & 1);
+    load_v(j + 1, (j + 1) & 1);
+    bf16x8 ring[kDist + 1];
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
+    for (int t = 0; t < kDist; ++t) ring[t] = operand(t);
+    f32x16 sn[C::NB];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[nb][r] = 0.f;
-#pragma unroll
-        for (int kc = 0; kc < C::KC; ++kc) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              ks + (nb * 32 + l32) * C::KS + kc * 8 + g * 4);
-          sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc],
-                                                             sacc[nb], 0, 0, 0);
-        }
-      }
-
-      // Mask keys past N, and (causal) keys after the query row.
-      // Accumulator r of block nb is key 32nb + 8(r/4) + 4g + (r%4).
-      const bool need_mask =
-          (key0 + kBlockN > N) || (CAUSAL && key0 + kBlockN - 1 > row0 + wave * 32);
-      if (need_mask) {
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + nb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-            const bool ok = key < N && (!CAUSAL || key <= my_row);
-            sacc[nb][r] = ok ? sacc[nb][r] : -INFINITY;
-          }
-      }
-
-      // Online softmax (log2 domain, scale folded into one FMA).
-      float mx = -INFINITY;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
-      mx = xhalf_max(mx);
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float rsum = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p =
-              __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[nb][r], scale_log2, -m_use));
-          sacc[nb][r] = p;
-          rsum += p;
-        }
-      l_run = l_run * alpha + rsum;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < C::DB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-
-      // O^T += V^T P^T, 16 keys per MFMA.
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) {
+    for (int nb = 0; nb < C::NB; ++nb) sn[nb] = f32x16{};
+    float pf[C::NC][8];
+    uint32_t pk[C::NC][4];
+    float mx = -INFINITY;
+    auto step = [&](int st) {
+      if (st < TS::EXP_STEPS) {
+        const int c = st / TS::STEPS_PER_CHUNK, k = st % TS::STEPS_PER_CHUNK;
         const int nb = c >> 1, r0 = (c & 1) * 8;
-        u32x4 pw;
-        pw.x = pack_bf16x2(sacc[nb][r0 + 0], sacc[nb][r0 + 1]);
-        pw.y = pack_bf16x2(sacc[nb][r0 + 2], sacc[nb][r0 + 3]);
-        pw.z = pack_bf16x2(sacc[nb][r0 + 4], sacc[nb][r0 + 5]);
-        pw.w = pack_bf16x2(sacc[nb][r0 + 6], sacc[nb][r0 + 7]);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              vs + (db * 32 + l32) * C::VS + c * 8 + g * 4);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db],
-                                                             0, 0, 0);
+        if (k < 8) {
+          pf[c][k] = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(s_cur[nb][r0 + k], scale_log2, -m_use));
+        } else if (k < 12) {
+          const int w = k - 8;
+          pk[c][w] = pack_bf16x2(pf[c][2 * w], pf[c][2 * w + 1]);
+        } else {
+          const int w = k - 12;
+          l_run += pf[c][2 * w] + pf[c][2 * w + 1];
         }
+      } else if (st < TS::EXP_STEPS + TS::MAX_STEPS) {
+        const int i = st - TS::EXP_STEPS;
+        const int nb = i / 8, r = (i % 8) * 2;
+        mx = fmaxf(fmaxf(mx, sn[nb][r]), sn[nb][r + 1]);
       }
+    };
+#pragma unroll
+    for (int t = 0; t < TS::T; ++t) {
+      if (t + kDist < TS::T) ring[(t + kDist) % (kDist + 1)] = operand(t + kDist);
+      const bf16x8 a = ring[t % (kDist + 1)];
+      if (t < TS::NS) {
+        const int nb = t / C::KC, kc = t % C::KC;
+        sn[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], sn[nb], 0, 0, 0);
+      } else {
+        const int u = t - TS::NS, c = u / C::DB, db = u % C::DB;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]}),
+            oacc[db], 0, 0, 0);
+      }
+#pragma unroll
+      for (int st = 0; st < TS::STEPS; ++st)
+        if (TS::bundle(st) == t) step(st);
+      __builtin_amdgcn_sched_barrier(0);
     }
-
-    if (has_next) store_tile(stage ^ 1);
+    mx_cur = xhalf_max(mx) * scale_log2;
+    wait_loads();
     __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) s_cur[nb] = sn[nb];
+  }
+  // Tail: masked tiles (ragged N, causal diagonal) and the last tile.
+  for (; j < n_tiles; ++j) {
+    const bool has1 = j + 1 < n_tiles;
+    const bool has2 = j + 2 < n_tiles;
+    if (has2) load_k(j + 2, j & 1);
+    if (has1) load_v(j + 1, (j + 1) & 1);
+    const int key0 = j * kBlockN;
+    // A wave whose last row precedes a tile has nothing to do for it.
+    const bool act_next = has1 && (!CAUSAL || key0 + kBlockN <= wave_row_last);
+    const bool act_cur = !CAUSAL || key0 <= wave_row_last;
+    if (act_next) scores((j + 1) & 1, s_next);
+    if (act_cur) {
+      if ((key0 + kBlockN > N) ||
+          (CAUSAL && key0 + kBlockN - 1 > wave_row_first))
+        mask(s_cur, key0);
+      const float m_use = update_max(tile_max(s_cur));
+      exp_pv(s_cur, m_use, j & 1);
+    }
+    wait_loads();
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) s_cur[nb] = s_next[nb];
   }
 
   // ---- epilogue: O /= l, lse = ln2 * (m + log2 l)
@@ -366,11 +519,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int col = db * 32 + rr * 8 + g * 4;
-      if (col < d) {
+      if (FULL_D || col < dd) {
         u32x2 w;
         w.x = pack_bf16x2(oacc[db][rr * 4 + 0] * inv, oacc[db][rr * 4 + 1] * inv);
         w.y = pack_bf16x2(oacc[db][rr * 4 + 2] * inv, oacc[db][rr * 4 + 3] * inv);
-        __builtin_amdgcn_raw_buffer_store_b64(w, o_rs, (my_row * d + col) * 2, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(
+            w, o_rs, (uint32_t)(my_row * dd + col) * 2u, 0, 0);
       }
     }
   if (lse != nullptr && g == 0 && my_row < N) {

@@ -95,17 +95,32 @@ int resolve_xcd(int* out) {
   return ATTN_OK;
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch(const void* q, const void* k, const void* v, void* o,
+template <int D, bool CAUSAL, bool FULL_D>
+hipError_t launch_one(const void* q, const void* k, const void* v, void* o,
                   float* lse, int B, int H_Q, int H_KV, int N, int d, int M,
                   int W, int mapping, int X, float scale_log2,
                   hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(W), dim3(kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, FULL_D>), dim3(W), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
                      lse, B, H_Q, H_KV, N, d, M, mapping, X, scale_log2);
   return hipGetLastError();
+}
+
+// Picks the instantiation: padded head dim D (64 or 128), causal, and whether
+// d == D (no padded columns to zero-fill).
+template <int D>
+hipError_t launch(const void* q, const void* k, const void* v, void* o,
+                  float* lse, int B, int H_Q, int H_KV, int N, int d, int M,
+                  int W, int causal, int mapping, int X, float scale_log2,
+                  hipStream_t s) {
+  const bool full = (d == D);
+  if (causal)
+    return full ? launch_one<D, true, true>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W, mapping, X, scale_log2, s)
+                : launch_one<D, true, false>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W, mapping, X, scale_log2, s);
+  return full ? launch_one<D, false, true>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W, mapping, X, scale_log2, s)
+              : launch_one<D, false, false>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W, mapping, X, scale_log2, s);
 }
 
 // Placement probe: one wave per workgroup; lane 0 records the XCC id the
@@ -149,18 +164,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   const float scale_log2 =
       (float)(1.4426950408889634 / std::sqrt((double)d));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (d <= 64) {
-    e = causal ? launch<64, true>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W,
-                                  mapping, X, scale_log2, s)
-               : launch<64, false>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W,
-                                   mapping, X, scale_log2, s);
-  } else {
-    e = causal ? launch<128, true>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W,
-                                   mapping, X, scale_log2, s)
-               : launch<128, false>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W,
-                                    mapping, X, scale_log2, s);
-  }
+  const hipError_t e =
+      (d <= 64) ? launch<64>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W, causal,
+                             mapping, X, scale_log2, s)
+                : launch<128>(q, k, v, o, lse, B, H_Q, H_KV, N, d, M, W, causal,
+                              mapping, X, scale_log2, s);
   if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
   return ATTN_OK;
 }
