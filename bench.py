@@ -163,6 +163,157 @@ def cpu_baseline(q, k, v, causal, budget_s: float):
     }
 
 
+PROFILE_PASSES = {
+    # pass name: counters (each pass is its own rocprofv3 run)
+    "l2": ["TCC_HIT_sum", "TCC_MISS_sum"],
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+    "mfma": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+             "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+}
+
+
+def profile_commands(workload: str, out: str):
+    """The rocprofv3 runs whose output --summarize-profile reads."""
+    bench = "python3 /root/repo/bench.py"
+    one = f"{bench} --workload {workload} --steps 1 --warmup 0 --modes 0,1,2,3 --no-cpu-baseline"
+    cmds = {"trace": (f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/trace -o trace -- "
+                      f"{bench} --workload {workload} --steps 2 --warmup 1 --modes 0,1,2,3 --no-cpu-baseline")}
+    for name, ctrs in PROFILE_PASSES.items():
+        cmds[name] = (f"rocprofv3 --pmc {' '.join(ctrs)} --output-format csv -d {out}/{name} -o {name} -- {one}")
+    for name in ("fetch", "write"):
+        cmds["copy_" + name] = (f"rocprofv3 --pmc {' '.join(PROFILE_PASSES[name])} --output-format csv "
+                                f"-d {out}/copy_{name} -o copy_{name} -- {bench} --copy-calibration")
+    return cmds
+
+
+def _read_counters(path, kernel_substr):
+    """{dispatch_id: {counter: value summed over dimensions}} and durations."""
+    import csv
+    vals, dur = {}, {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel_substr not in r["Kernel_Name"]:
+                continue
+            dk = int(r["Dispatch_Id"])
+            vals.setdefault(dk, {})
+            vals[dk][r["Counter_Name"]] = vals[dk].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            dur[dk] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    return [vals[k] for k in sorted(vals)], [dur[k] for k in sorted(dur)]
+
+
+def _recorded_commands(directory: str, workload: str):
+    """The commands the profiling run executed: `commands.txt` written there
+    by --print-profile-commands, else the commands for that directory."""
+    path = os.path.join(directory, "commands.txt")
+    if os.path.exists(path):
+        with open(path) as f:
+            cmds = [line.strip() for line in f if line.strip()]
+        return dict(zip(profile_commands(workload, "X").keys(), cmds))
+    return profile_commands(workload, os.path.abspath(directory))
+
+
+def summarize_profile(directory: str, workload: str):
+    """Turns the rocprofv3 CSVs of profile_commands() into profiles/ files."""
+    import csv
+    import glob
+    B, H_Q, H_KV, N, d, causal = WORKLOADS[workload]
+    flops = attn_flops(B, H_Q, N, d, causal)
+
+    def one(pass_name, kernel="attn_fwd_kernel"):
+        files = glob.glob(os.path.join(directory, pass_name, "*_counter_collection.csv"))
+        if not files:
+            raise SystemExit(f"missing {pass_name} counters under {directory}")
+        return _read_counters(files[0], kernel)
+
+    # Copy calibration: a plain 1 GiB device copy; its last dispatch is timed.
+    cal = {}
+    for name, ctr in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        v, _ = one("copy_" + name, kernel="copyBuffer")
+        kib = v[-1][ctr]
+        cal[ctr] = (1 << 30) / (kib * 1024.0)
+    l2, durs = one("l2")
+    fe, _ = one("fetch")
+    wr, _ = one("write")
+    mf, mdur = one("mfma")
+    n_modes = len(l2)
+    if not (len(fe) == len(wr) == len(mf) == n_modes == 4):
+        raise SystemExit("expected one dispatch per mapping mode in every pass")
+    # Kernel-trace statistics (average duration of the attention kernel).
+    trace = glob.glob(os.path.join(directory, "trace", "*_kernel_stats.csv"))
+    stats = []
+    if trace:
+        with open(trace[0]) as f:
+            stats = [r for r in csv.DictReader(f)]
+    unique = (2 * H_Q + 2 * H_KV) * B * N * d * 2 + 4 * B * H_Q * N
+    modes = {}
+    for m in range(n_modes):
+        hit, miss = l2[m]["TCC_HIT_sum"], l2[m]["TCC_MISS_sum"]
+        fetch_b = fe[m]["FETCH_SIZE"] * 1024.0 * cal["FETCH_SIZE"]
+        write_b = wr[m]["WRITE_SIZE"] * 1024.0 * cal["WRITE_SIZE"]
+        gui = mf[m]["GRBM_GUI_ACTIVE"]
+        # GRBM_GUI_ACTIVE sums the busy cycles of every XCD.
+        clock = gui / 8.0 / mdur[m] / 1e9
+        simd_cycles = gui / 8.0 * 1024  # 256 CUs x 4 SIMDs
+        modes[MODE_NAMES[m]] = {
+            "l2_hit_pct": round(100.0 * hit / (hit + miss), 2),
+            "fetch_bytes": fetch_b, "write_bytes": write_b,
+            "hbm_bytes": fetch_b + write_b,
+            "fetch_over_unique": round(fetch_b / unique, 2),
+            "mfma_busy_pct": round(100.0 * mf[m]["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles, 2),
+            "mfma_flops_counted": mf[m]["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0,
+            "clock_ghz": round(clock, 3),
+            "kernel_ms_counter_run": round(durs[m] * 1e3, 2),
+        }
+    data = {
+        "kernel": "attn_numa::attn_fwd_kernel",
+        "kernel_hash": kernel_hash(),
+        "workload": workload, "description": describe(workload),
+        "algorithmic_flops": flops, "unique_bytes": unique,
+        "calibration": {"copy_bytes": 1 << 30, "scale": cal},
+        "modes": modes,
+        "commands": _recorded_commands(directory, workload),
+    }
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"counters_attn_fwd_{workload}.json"), "w") as f:
+        json.dump(data, f, indent=1)
+    lines = [f"# attn_fwd_kernel, {describe(workload)}", "",
+             f"Kernel source hash {data['kernel_hash']} (sha256 of the kernel sources, first 16 hex).",
+             f"Algorithmic work {flops / 1e12:.1f} TFLOP per call; unique Q+K+V+O+lse footprint "
+             f"{unique / 2**30:.2f} GiB.", "",
+             "## rocprofv3 --kernel-trace --stats", "",
+             "| kernel | calls | average ms | min ms | max ms |", "|---|---|---|---|---|"]
+    for r in stats:
+        if "attn_fwd_kernel" in r["Name"]:
+            lines.append(f"| {r['Name'].split('(')[0]} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.2f} | "
+                         f"{float(r['MinNs']) / 1e6:.2f} | {float(r['MaxNs']) / 1e6:.2f} |")
+    lines += ["", "(the trace mixes the four mapping modes, 3 calls each: see the per-mode table)", "",
+              "## Counters per mapping mode (one dispatch each)", "",
+              "| mode | L2 hit % | HBM read GB | HBM write GB | read / unique | MFMA busy % | clock GHz | kernel ms | TFLOP/s |",
+              "|---|---|---|---|---|---|---|---|---|"]
+    for name, mm in modes.items():
+        lines.append(f"| {name} | {mm['l2_hit_pct']} | {mm['fetch_bytes'] / 1e9:.1f} | {mm['write_bytes'] / 1e9:.2f} | "
+                     f"{mm['fetch_over_unique']} | {mm['mfma_busy_pct']} | {mm['clock_ghz']} | "
+                     f"{mm['kernel_ms_counter_run']} | {flops / (mm['kernel_ms_counter_run'] / 1e3) / 1e12:.0f} |")
+    lines += ["", f"HBM bytes are FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what the same "
+              f"counters read for a plain 1 GiB device copy: read x{cal['FETCH_SIZE']:.3f}, "
+              f"write x{cal['WRITE_SIZE']:.3f}. They count L2-to-fabric traffic, so reads served by "
+              f"the Infinity Cache are included.", "",
+              "MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
+              "clock = GRBM_GUI_ACTIVE / 8 / kernel duration.", "", "## Commands", ""]
+    lines.append("Each pass is its own process, run as `cd /tmp && export TMPDIR=/tmp && <command>` "
+                 "with the repository at /root/repo; then "
+                 f"`python3 bench.py --workload {workload} --summarize-profile DIR` (DIR: the directory "
+                 "the -d paths below share) "
+                 "wrote this file.")
+    lines.append("")
+    for name, cmd in data["commands"].items():
+        lines.append(f"- {name}: `{cmd}`")
+    with open(os.path.join(PROFILES, f"attn_fwd_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({k: v for k, v in data.items() if k != "commands"}, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -178,7 +329,19 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (twice), the "
                          "reference for scaling HBM byte counters")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="summarize rocprofv3 CSV output under DIR (made by the "
+                         "commands --print-profile-commands lists) into profiles/")
+    ap.add_argument("--print-profile-commands", metavar="OUT",
+                    help="print the rocprofv3 commands for --workload, output under OUT")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.workload)
+        return
+    if args.print_profile_commands:
+        for cmd in profile_commands(args.workload, args.print_profile_commands).values():
+            print(cmd)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
