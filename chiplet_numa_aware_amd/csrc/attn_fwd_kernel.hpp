@@ -44,6 +44,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "wg_map.hpp"
 
 namespace attn_numa {
@@ -84,6 +87,25 @@ __device__ __forceinline__ void load_lds_b128(u32x4 desc, uint32_t voff,
       :
       : "s"(lds_byte), "v"(voff), "s"(desc)
       : "memory", "m0");
+}
+
+// f(std::integral_constant<int, i>{}) for i = 0..N-1, expanded at compile
+// time (no reliance on loop unrolling), so every index inside is a constant.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Pins a value's computation to this point of the instruction stream: the
+// empty asm is ordered with the schedule barriers and the loads, so work that
+// reads or writes `x` here cannot be hoisted or sunk into another bundle.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
 }
 
 // lo16(a) | lo16(b) << 16 and hi16(a) | hi16(b) << 16.
@@ -244,12 +266,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   // are below 2^31).
   const uint32_t lds_base = (uint32_t)(uintptr_t)(
       (__attribute__((address_space(3))) char*)lds_b);
+  auto load_one = [&](u32x4 desc, int tile, int lds_byte, int i) {
+    load_lds_b128(desc, ld_off[i] + (uint32_t)tile * tile_bytes,
+                  lds_base + lds_byte + (i * 4 + wave) * 1024);
+  };
   auto load_tile = [&](u32x4 desc, int tile, int lds_byte) {
-    const uint32_t base = (uint32_t)tile * tile_bytes;
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
-      load_lds_b128(desc, ld_off[i] + base,
-                    lds_base + lds_byte + (i * 4 + wave) * 1024);
+    for (int i = 0; i < C::LOADS; ++i) load_one(desc, tile, lds_byte, i);
   };
   auto load_k = [&](int tile, int buf) { load_tile(k_desc, tile, buf * C::TILE_B); };
   auto load_v = [&](int tile, int buf) { load_tile(v_desc, tile, kVBase + buf * C::TILE_B); };
@@ -420,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   float mx_cur = tile_max(s_cur);  // used only while tiles are steady
   using TS = TileSchedule<D>;
   static_assert(TS::valid(), "tile schedule breaks a data dependency");
-  constexpr int kDist = 3;  // LDS operand prefetch distance, in MFMAs
+  constexpr int kDist = 4;  // LDS operand prefetch distance, in MFMAs
   for (; j < n_steady; ++j) {
     const float m_use = update_max(mx_cur);
     // LDS operand of MFMA t: a K fragment (score MFMAs) or a V^T fragment.
@@ -430,56 +453,65 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       return v_operand(j & 1, u / C::DB, u % C::DB);
     };
     // K of tile j+2 (clamped to the last tile: a re-load that is never read)
-    // and V of tile j+1 go to the buffers this iteration does not read.
-    load_k((j + 2 < n_tiles) ? j + 2 : n_tiles - 1, j & 1);
-    load_v(j + 1, (j + 1) & 1);
+    // and V of tile j+1 go to the buffers this iteration does not read; the
+    // 2*LOADS load instructions are spread over the first bundles, one each,
+    // so that the texture units drain between them instead of stalling this
+    // wave's issue.
+    const int tk = (j + 2 < n_tiles) ? j + 2 : n_tiles - 1;
     bf16x8 ring[kDist + 1];
-#pragma unroll
-    for (int t = 0; t < kDist; ++t) ring[t] = operand(t);
+    static_for<kDist>([&](auto ti) {
+      constexpr int t = decltype(ti)::value;
+      ring[t] = operand(t);
+    });
     f32x16 sn[C::NB];
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) sn[nb] = f32x16{};
+    static_for<C::NB>([&](auto nbi) { sn[decltype(nbi)::value] = f32x16{}; });
     float pf[C::NC][8];
     uint32_t pk[C::NC][4];
     float mx = -INFINITY;
-    auto step = [&](int st) {
-      if (st < TS::EXP_STEPS) {
-        const int c = st / TS::STEPS_PER_CHUNK, k = st % TS::STEPS_PER_CHUNK;
-        const int nb = c >> 1, r0 = (c & 1) * 8;
-        if (k < 8) {
-          pf[c][k] = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(s_cur[nb][r0 + k], scale_log2, -m_use));
-        } else if (k < 12) {
-          const int w = k - 8;
+    auto step = [&](auto sti) {
+      constexpr int st = decltype(sti)::value;
+      if constexpr (st < TS::EXP_STEPS) {
+        constexpr int c = st / TS::STEPS_PER_CHUNK, k = st % TS::STEPS_PER_CHUNK;
+        constexpr int nb = c >> 1, r0 = (c & 1) * 8;
+        if constexpr (k < 8) {
+          float x = s_cur[nb][r0 + k];
+          pin(x);
+          pf[c][k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, scale_log2, -m_use));
+        } else if constexpr (k < 12) {
+          constexpr int w = k - 8;
           pk[c][w] = pack_bf16x2(pf[c][2 * w], pf[c][2 * w + 1]);
         } else {
-          const int w = k - 12;
+          constexpr int w = k - 12;
           l_run += pf[c][2 * w] + pf[c][2 * w + 1];
         }
-      } else if (st < TS::EXP_STEPS + TS::MAX_STEPS) {
-        const int i = st - TS::EXP_STEPS;
-        const int nb = i / 8, r = (i % 8) * 2;
+      } else {
+        constexpr int i = st - TS::EXP_STEPS;
+        constexpr int nb = i / 8, r = (i % 8) * 2;
         mx = fmaxf(fmaxf(mx, sn[nb][r]), sn[nb][r + 1]);
       }
     };
-#pragma unroll
-    for (int t = 0; t < TS::T; ++t) {
-      if (t + kDist < TS::T) ring[(t + kDist) % (kDist + 1)] = operand(t + kDist);
+    static_for<TS::T>([&](auto ti) {
+      constexpr int t = decltype(ti)::value;
+      if constexpr (t < C::LOADS)
+        load_one(k_desc, tk, (j & 1) * C::TILE_B, t);
+      else if constexpr (t < 2 * C::LOADS)
+        load_one(v_desc, j + 1, kVBase + ((j + 1) & 1) * C::TILE_B, t - C::LOADS);
+      if constexpr (t + kDist < TS::T) ring[(t + kDist) % (kDist + 1)] = operand(t + kDist);
       const bf16x8 a = ring[t % (kDist + 1)];
-      if (t < TS::NS) {
-        const int nb = t / C::KC, kc = t % C::KC;
+      if constexpr (t < TS::NS) {
+        constexpr int nb = t / C::KC, kc = t % C::KC;
         sn[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], sn[nb], 0, 0, 0);
       } else {
-        const int u = t - TS::NS, c = u / C::DB, db = u % C::DB;
+        constexpr int u = t - TS::NS, c = u / C::DB, db = u % C::DB;
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             a, __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]}),
             oacc[db], 0, 0, 0);
       }
-#pragma unroll
-      for (int st = 0; st < TS::STEPS; ++st)
-        if (TS::bundle(st) == t) step(st);
+      static_for<TS::STEPS>([&](auto sti) {
+        if constexpr (TS::bundle(decltype(sti)::value) == t) step(sti);
+      });
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     mx_cur = xhalf_max(mx) * scale_log2;
     wait_loads();
     __syncthreads();
