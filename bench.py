@@ -422,7 +422,7 @@ def main():
             "workload": describe(args.workload),
             "B": B, "H_Q": H_Q, "H_KV": H_KV, "N": N, "d": d,
             "causal": causal, "mapping": MODE_NAMES[headline],
-            "block_m": 128, "parallelism": "single GPU",
+            "block_m": attn.BLOCK_M, "parallelism": "single GPU",
         },
         "pct_peak": round(head["pct_peak"], 2),
         "l2_hit_pct": l2_hit,

@@ -7,6 +7,7 @@ entry points have the names of the C ABI in include/attn_numa.h:
 * ``attn_fwd(q, k, v, causal=False, mapping=3, o=None, lse=None)``
 * ``attn_wg_map(mapping, B, H_Q, H_KV, N, num_xcd)``
 * ``attn_num_xcd()``
+* ``attn_block_m()``
 * ``attn_probe_placement(mapping, B, H_Q, H_KV, N, out=None)``
 * ``attn_strerror(code)``
 
@@ -22,14 +23,13 @@ import numpy as np
 import torch  # first, so the library binds to the HIP runtime torch loaded
 
 __all__ = [
-    "AttnError", "attn_fwd", "attn_wg_map", "attn_num_xcd",
+    "AttnError", "attn_fwd", "attn_wg_map", "attn_num_xcd", "attn_block_m",
     "attn_probe_placement", "attn_strerror", "library_path", "load_library",
     "MAPPINGS", "row_blocks", "num_workgroups", "BLOCK_M",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "libattn_numa.so")
-BLOCK_M = 128
 
 # Mapping modes (ATTN_MAP_* in include/attn_numa.h).
 MAPPINGS = {
@@ -68,6 +68,8 @@ def load_library():
     lib.attn_wg_map.restype = i32
     lib.attn_num_xcd.argtypes = []
     lib.attn_num_xcd.restype = i32
+    lib.attn_block_m.argtypes = []
+    lib.attn_block_m.restype = i32
     lib.attn_probe_placement.argtypes = [i32] * 5 + [vp, vp]
     lib.attn_probe_placement.restype = i32
     lib.attn_strerror.argtypes = [i32]
@@ -85,8 +87,20 @@ def _check(code: int, where: str):
         raise AttnError(code, where)
 
 
+def attn_block_m() -> int:
+    """Query rows per workgroup (the row-block height)."""
+    return int(load_library().attn_block_m())
+
+
+def __getattr__(name):
+    # BLOCK_M is the library's row-block height, read when first asked for.
+    if name == "BLOCK_M":
+        return attn_block_m()
+    raise AttributeError(name)
+
+
 def row_blocks(N: int) -> int:
-    return -(-N // BLOCK_M)
+    return -(-N // attn_block_m())
 
 
 def num_workgroups(B: int, H_Q: int, N: int) -> int:

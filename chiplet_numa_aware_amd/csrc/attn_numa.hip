@@ -42,10 +42,13 @@ int check_shape(int B, int H_Q, int H_KV, int N, int* M_out, int* W_out) {
   return ATTN_OK;
 }
 
+constexpr int64_t kMaxHeadBytes = (int64_t(1) << 31) - (int64_t(1) << 16);
+
 int check_head_dim(int N, int d) {
   if (d <= 0 || d > 128 || (d % 8) != 0) return ATTN_E_HEAD_DIM;
-  // One head must fit a buffer resource (byte offsets are 32-bit signed).
-  if ((int64_t)N * d * 2 >= (int64_t(1) << 31)) return ATTN_E_SHAPE;
+  // One head must fit a buffer resource, with room for the out-of-range
+  // offset (2^31) plus a tile offset and an instruction offset below 2^32.
+  if ((int64_t)N * d * 2 > kMaxHeadBytes) return ATTN_E_SHAPE;
   return ATTN_OK;
 }
 
@@ -191,6 +194,8 @@ int attn_wg_map(int mapping, int B, int H_Q, int H_KV, int N, int num_xcd,
   return ATTN_OK;
 }
 
+int attn_block_m(void) { return kBlockM; }
+
 int attn_num_xcd(void) {
   int X = 0;
   int rc = resolve_xcd(&X);
@@ -222,7 +227,7 @@ const char* attn_strerror(int code) {
     case ATTN_E_NULL: return "a required pointer is NULL";
     case ATTN_E_SHAPE:
       return "bad shape (B, H_Q, H_KV, N must be > 0, H_Q % H_KV == 0, "
-             "B*H_Q*ceil(N/128) < 2^31, N*d*2 < 2^31, num_xcd >= 1)";
+             "B*H_Q*ceil(N/256) < 2^31, N*d*2 <= 2^31 - 2^16, num_xcd >= 1)";
     case ATTN_E_HEAD_DIM: return "unsupported head dim (need 8 <= d <= 128, d % 8 == 0)";
     case ATTN_E_MAPPING: return "mapping must be 0..3";
     case ATTN_E_ALIGN: return "device pointer not 16-byte aligned";

@@ -40,7 +40,7 @@ enum Mapping : int {
   kSwizzledHeadFirst = 3,
 };
 
-constexpr int kBlockM = 128;  // query rows per workgroup (row-block height)
+constexpr int kBlockM = 256;  // query rows per workgroup (row-block height)
 
 struct WgCoord {
   uint32_t b, h, m;

@@ -52,8 +52,8 @@ extern "C" {
  * attn_fwd: attention forward pass.
  *
  * Passage: digest page §4 equation (the result) and §3 Figure 4 (the
- * row-block tiling: one workgroup per 128 query rows of a head, reading all
- * of that head's K and V).
+ * row-block tiling: one workgroup per attn_block_m() = 256 query rows of a
+ * head, reading all of that head's K and V).
  *
  *   q    device, bf16 [B][H_Q][N][d], contiguous, read only
  *   k    device, bf16 [B][H_KV][N][d], contiguous, read only
@@ -63,8 +63,8 @@ extern "C" {
  *        logsumexp of the scaled (and masked) scores of each query row
  *   B, H_Q, H_KV, N, d   shape; H_Q % H_KV == 0; query head h reads KV head
  *        h / (H_Q / H_KV); 8 <= d <= 128 with d % 8 == 0 (d <= 64 runs a
- *        64-wide tile, else a 128-wide one); B*H_Q*ceil(N/128) < 2^31 and
- *        N*d*2 < 2^31 bytes per head
+ *        64-wide tile, else a 128-wide one); B*H_Q*ceil(N/256) < 2^31 and
+ *        N*d*2 <= 2^31 - 2^16 bytes per head
  *   causal  0: every key; 1: query row i sees keys 0..i (top-left aligned)
  *   mapping ATTN_MAP_* (0..3); the XCD count used is attn_num_xcd()
  *   stream  hipStream_t or NULL
@@ -86,7 +86,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * Passage: digest page §2 Q1 (dispatch to XCD w mod X), §2 Q2 and §7
  * Figures 3 and 11 (the swizzles), §3 Figure 10.
  *
- *   out_host  host, int32 [W][3], W = B*H_Q*ceil(N/128); row w receives the
+ *   out_host  host, int32 [W][3], W = B*H_Q*ceil(N/attn_block_m()); row w
+ *             receives the
  *             (batch, query head, row block) that workgroup w computes when
  *             the chip has num_xcd XCDs.  Caller-owned.
  *   num_xcd   >= 1 (pass attn_num_xcd() for the device's value)
@@ -96,6 +97,15 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  */
 int attn_wg_map(int mapping, int B, int H_Q, int H_KV, int N, int num_xcd,
                 int32_t* out_host);
+
+/*
+ * attn_block_m: query rows per workgroup (the row-block height, 256), so
+ * that a caller can size the tables of attn_wg_map and attn_probe_placement:
+ * W = B * H_Q * ceil(N / attn_block_m()).  The pages tile rows by 128
+ * (digest page §4); 256 rows per workgroup halve the K/V tile traffic per
+ * CU on MI355X.  Needs no GPU.
+ */
+int attn_block_m(void);
 
 /*
  * attn_num_xcd: XCDs of the current device (8 on MI355X in SPX mode), the

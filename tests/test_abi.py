@@ -34,10 +34,31 @@ def _declared_codes():
 
 def test_library_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert set(names) == {"attn_fwd", "attn_wg_map", "attn_num_xcd",
+    assert set(names) == {"attn_fwd", "attn_wg_map", "attn_num_xcd", "attn_block_m",
                           "attn_probe_placement", "attn_strerror"}
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_block_m_sizes_the_tables(lib):
+    """attn_block_m needs no GPU and sizes attn_wg_map's table."""
+    bm = lib.attn_block_m()
+    assert bm == attn.BLOCK_M and bm % 64 == 0
+    for N in (1, bm - 1, bm, bm + 1, 5 * bm + 7):
+        assert attn.attn_wg_map(3, 2, 4, 2, N, 8).shape == (2 * 4 * (-(-N // bm)), 3)
+
+
+def test_head_size_limit(lib):
+    """One head may hold at most 2^31 - 2^16 bytes (the range-checked buffer
+    offsets stay below 2^32); the check runs before any device query."""
+    c = _declared_codes()
+    limit = (1 << 31) - (1 << 16)
+    assert limit % 256 == 0
+    kw = dict(B=1, H_Q=1, H_KV=1, d=128, causal=0)
+    assert _fwd(lib, N=limit // 256 + 1, mapping=3, **kw) == c["ATTN_E_SHAPE"]
+    # At the limit the shape passes and the (invalid) mapping is reported:
+    # validation ends before anything could launch on the fake pointers.
+    assert _fwd(lib, N=limit // 256, mapping=7, **kw) == c["ATTN_E_MAPPING"]
 
 
 def test_strerror_covers_every_code(lib):
@@ -108,13 +129,13 @@ def _shapes():
 def test_host_wg_map_equals_oracle(mode):
     for B, H_Q, H_KV, N, X in _shapes():
         got = attn.attn_wg_map(mode, B, H_Q, H_KV, N, X)
-        W = oracle.num_workgroups(B, H_Q, N)
+        W = oracle.num_workgroups(B, H_Q, N, attn.BLOCK_M)
         assert got.shape == (W, 3)
         if W > 20000:  # spot-check the large tables
             idx = np.random.default_rng(W).integers(0, W, 4000)
         else:
             idx = np.arange(W)
-        exp = np.array([oracle.wg_map(mode, int(w), B, H_Q, N, X) for w in idx],
+        exp = np.array([oracle.wg_map(mode, int(w), B, H_Q, N, X, attn.BLOCK_M) for w in idx],
                        dtype=np.int32).reshape(-1, 3)
         assert np.array_equal(got[idx], exp), (mode, B, H_Q, H_KV, N, X)
 
@@ -123,7 +144,7 @@ def test_host_wg_map_is_bijection_on_headline_shape():
     for mode in range(4):
         t = attn.attn_wg_map(mode, 1, 128, 128, 131072, 8).astype(np.int64)
         key = (t[:, 0] * 128 + t[:, 1]) * 1024 + t[:, 2]
-        assert np.unique(key).size == t.shape[0] == 131072
+        assert np.unique(key).size == t.shape[0] == 128 * (131072 // attn.BLOCK_M)
 
 
 def test_num_xcd_env_override(monkeypatch):
