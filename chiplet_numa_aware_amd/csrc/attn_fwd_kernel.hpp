@@ -1,6 +1,6 @@
 // FlashAttention-2 style attention forward for gfx950 (MI355X).
 //
-// One workgroup computes one (batch, query head, 128-row block), streaming
+// One workgroup computes one (batch, query head, 256-row block), streaming
 // every K/V tile of its KV head with an online softmax ("Optimizing Attention
 // on GPUs by Exploiting GPU Architectural NUMA Effects", digest page, §3
 // Figure 4 and the §4 equation).  Which block a workgroup takes comes from

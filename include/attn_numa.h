@@ -5,8 +5,9 @@
  * The operation is scaled dot-product attention, S = Q K^T, P = softmax(S /
  * sqrt(d)), O = P V, per head ("Optimizing Attention on GPUs by Exploiting GPU
  * Architectural NUMA Effects", digest page, §4 equation), computed by one
- * workgroup per (batch, query head, 128-row block) that streams all of that
- * head's K and V with an online softmax (same page, §3 Figure 4).  Which
+ * workgroup per (batch, query head, row block of attn_block_m() rows) that
+ * streams all of that head's K and V with an online softmax (same page, §3
+ * Figure 4).  Which
  * workgroup takes which row block is set by one of four workgroup-ID remaps
  * (same page, §2 Q2, §3 Figure 10 and the before/after table, §7 Figures 3
  * and 11).
