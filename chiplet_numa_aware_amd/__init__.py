@@ -5,6 +5,9 @@ the library's HIP kernels.  torch provides device memory and streams.  The
 entry points have the names of the C ABI in include/attn_numa.h:
 
 * ``attn_fwd(q, k, v, causal=False, mapping=3, o=None, lse=None)``
+* ``attn_fwd_split(q, k, v, causal=False, num_splits=1, mapping=3, ...)``
+* ``attn_split_chunk(N_kv, num_splits)``
+* ``attn_merge(o_parts, lse_parts, o=None, lse=None)``
 * ``attn_wg_map(mapping, B, H_Q, H_KV, N, num_xcd)``
 * ``attn_num_xcd()``
 * ``attn_block_m()``
@@ -23,7 +26,8 @@ import numpy as np
 import torch  # first, so the library binds to the HIP runtime torch loaded
 
 __all__ = [
-    "AttnError", "attn_fwd", "attn_wg_map", "attn_num_xcd", "attn_block_m",
+    "AttnError", "attn_fwd", "attn_fwd_split", "attn_split_chunk", "attn_merge",
+    "attn_wg_map", "attn_num_xcd", "attn_block_m",
     "attn_probe_placement", "attn_strerror", "library_path", "load_library",
     "MAPPINGS", "row_blocks", "num_workgroups", "BLOCK_M",
 ]
@@ -64,6 +68,12 @@ def load_library():
     vp, i32 = ctypes.c_void_p, ctypes.c_int
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp] + [i32] * 7 + [vp]
     lib.attn_fwd.restype = i32
+    lib.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp] + [i32] * 8 + [vp, vp, i32, vp]
+    lib.attn_fwd_split.restype = i32
+    lib.attn_split_chunk.argtypes = [i32, i32]
+    lib.attn_split_chunk.restype = i32
+    lib.attn_merge.argtypes = [vp, vp] + [i32] * 5 + [vp, vp, vp]
+    lib.attn_merge.restype = i32
     lib.attn_wg_map.argtypes = [i32] * 6 + [vp]
     lib.attn_wg_map.restype = i32
     lib.attn_num_xcd.argtypes = []
@@ -155,6 +165,99 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                           B, H_Q, H_KV, N, d, int(bool(causal)),
                           _mapping_id(mapping), _stream_handle(stream, q.device))
     _check(rc, "attn_fwd")
+    return o, lse
+
+
+def _check_bf16(name, t):
+    if not isinstance(t, torch.Tensor) or t.dim() != 4:
+        raise ValueError(f"{name} must be a 4-D tensor")
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bf16 GPU tensor")
+
+
+def _check_f32(name, t, shape):
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape)
+            or t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
+        raise ValueError(f"{name} must be a contiguous fp32 GPU tensor of shape {tuple(shape)}")
+
+
+def attn_split_chunk(N_kv: int, num_splits: int) -> int:
+    """Keys per split of attn_fwd_split (host, no GPU)."""
+    rc = load_library().attn_split_chunk(int(N_kv), int(num_splits))
+    if rc < 0:
+        raise AttnError(rc, "attn_split_chunk")
+    return rc
+
+
+def attn_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   causal: bool = False, num_splits: int = 1, mapping=3,
+                   o: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                   o_ws: torch.Tensor | None = None, lse_ws: torch.Tensor | None = None,
+                   need_lse: bool = True, stream: torch.cuda.Stream | None = None):
+    """Attention of q [B,H_Q,N_q,d] over k, v [B,H_KV,N_kv,d], keys split in
+    ``num_splits`` ranges and merged: returns (o, lse).  Causal is
+    bottom-right aligned.  For num_splits > 1 the fp32 workspaces o_ws
+    [S,B,H_Q,N_q,d] and lse_ws [S,B,H_Q,N_q] are allocated when not given;
+    after the call they hold each split's partial result."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(name, t)
+    B, H_Q, N_q, d = q.shape
+    H_KV, N_kv = k.shape[1], k.shape[2]
+    if k.shape != (B, H_KV, N_kv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H_KV, N_kv, d] with q's B and d")
+    S = int(num_splits)
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous():
+        raise ValueError("o must be a contiguous bf16 tensor shaped like q")
+    if lse is None and need_lse:
+        lse = torch.empty((B, H_Q, N_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_f32("lse", lse, (B, H_Q, N_q))
+    if S > 1:
+        if o_ws is None:
+            o_ws = torch.empty((S, B, H_Q, N_q, d), dtype=torch.float32, device=q.device)
+        if lse_ws is None:
+            lse_ws = torch.empty((S, B, H_Q, N_q), dtype=torch.float32, device=q.device)
+        _check_f32("o_ws", o_ws, (S, B, H_Q, N_q, d))
+        _check_f32("lse_ws", lse_ws, (S, B, H_Q, N_q))
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        rc = lib.attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr() if lse is not None else None,
+                                B, H_Q, H_KV, N_q, N_kv, d, int(bool(causal)), S,
+                                o_ws.data_ptr() if S > 1 else None,
+                                lse_ws.data_ptr() if S > 1 else None,
+                                _mapping_id(mapping), _stream_handle(stream, q.device))
+    _check(rc, "attn_fwd_split")
+    return o, lse
+
+
+def attn_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,
+               o: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+               need_lse: bool = True, stream: torch.cuda.Stream | None = None):
+    """Merge partial results o_parts fp32 [S,B,H_Q,N_q,d], lse_parts fp32
+    [S,B,H_Q,N_q] into (o bf16 [B,H_Q,N_q,d], lse fp32 [B,H_Q,N_q])."""
+    if o_parts.dim() != 5:
+        raise ValueError("o_parts must be [S, B, H_Q, N_q, d]")
+    S, B, H_Q, N_q, d = o_parts.shape
+    _check_f32("o_parts", o_parts, (S, B, H_Q, N_q, d))
+    _check_f32("lse_parts", lse_parts, (S, B, H_Q, N_q))
+    if o is None:
+        o = torch.empty((B, H_Q, N_q, d), dtype=torch.bfloat16, device=o_parts.device)
+    _check_bf16("o", o)
+    if o.shape != (B, H_Q, N_q, d):
+        raise ValueError("o must be [B, H_Q, N_q, d]")
+    if lse is None and need_lse:
+        lse = torch.empty((B, H_Q, N_q), dtype=torch.float32, device=o_parts.device)
+    if lse is not None:
+        _check_f32("lse", lse, (B, H_Q, N_q))
+    lib = load_library()
+    with torch.cuda.device(o_parts.device):
+        rc = lib.attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, B, H_Q, N_q, d,
+                            o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                            _stream_handle(stream, o_parts.device))
+    _check(rc, "attn_merge")
     return o, lse
 
 

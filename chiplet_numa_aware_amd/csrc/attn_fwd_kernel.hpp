@@ -4,10 +4,14 @@
 // every K/V tile of its KV head with an online softmax ("Optimizing Attention
 // on GPUs by Exploiting GPU Architectural NUMA Effects", digest page, §3
 // Figure 4 and the §4 equation).  Which block a workgroup takes comes from
-// wg_map.hpp.
+// wg_map.hpp.  With split-KV the keys are cut into num_splits tile-aligned
+// ranges and each workgroup covers one (row block, range), writing a partial
+// result (O normalised over the range, its lse) that a merge kernel combines
+// ("Fused Grouped-Query Attention" page, the decode reduction of per-shard
+// partial results).
 //
-// Work inside a workgroup (128 threads = 2 waves of 64; one wave per SIMD,
-// two workgroups per CU):
+// Work inside a workgroup (256 threads = 4 waves of 64; one wave per SIMD,
+// one workgroup per CU):
 //   * wave w owns query rows [64w, 64w+64) of the block as two 32-row query
 //     blocks qb; lane l owns rows 64w + 32qb + (l mod 32); lanes l and l^32
 //     share those rows and split their keys.
@@ -43,9 +47,9 @@
 //     once at the end.
 //
 // Global memory is read and written through buffer resources that cover one
-// head (at most 2^31 bytes): rows past N read as zero and stores past N are
-// dropped, so ragged N needs no branches; padded head-dim columns use an
-// offset that is always out of range.  All 64-bit address arithmetic is
+// head (at most 2^31 - 2^16 bytes): rows past the end read as zero and bf16
+// stores past it are dropped, so ragged lengths need no branches; padded
+// head-dim columns use an offset that is always out of range.  All 64-bit address arithmetic is
 // scalar.
 #pragma once
 
@@ -298,8 +302,9 @@ template <int D, bool CAUSAL, bool FULL_D>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int B, int H_Q, int H_KV, int N, int d, int M,
-    int mapping, int num_xcd, float scale_log2) {
+    float* __restrict__ lse, int B, int H_Q, int H_KV, int N_q, int N_kv, int d,
+    int M_q, int kv_chunk, int num_splits, float* __restrict__ o_ws,
+    float* __restrict__ lse_ws, int mapping, int num_xcd, float scale_log2) {
   using C = TileCfg<D>;
   using TS = TileSchedule<D>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[C::LDS_B / 4];
@@ -313,30 +318,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   const int g = lane >> 5;     // lane half: which 8 of 16 MFMA k values
   const int l32 = lane & 31;   // query row within a query block / MFMA column
 
-  const WgCoord wc = wg_map(mapping, blockIdx.x, B, H_Q, M, num_xcd);
+  // The remap sees M_q * num_splits row blocks per head: m' = split * M_q +
+  // row block, so the workgroups of one key range are adjacent.
+  const WgCoord wc = wg_map(mapping, blockIdx.x, B, H_Q, M_q * num_splits, num_xcd);
   const int kvh = (int)wc.h / (H_Q / H_KV);
-  const int row0 = (int)wc.m * kBlockM;
+  const int split = (int)wc.m / M_q;
+  const int row0 = ((int)wc.m - split * M_q) * kBlockM;
+  // Keys of this workgroup: [kv_begin, kv_end), tile-aligned.  Causal: query
+  // row r sees keys <= r + off (bottom-right aligned; off = 0 when N_q == N_kv).
+  const int kv_begin = split * kv_chunk;
+  const int kv_end = min(kv_begin + kv_chunk, N_kv);
+  const int off = CAUSAL ? N_kv - N_q : 0;
 
   // Row length in elements: the compile-time D when d == D, so that every
   // per-lane offset below is a constant multiple and folds into immediates.
   const int dd = FULL_D ? D : d;
-  const uint32_t head_elems = (uint32_t)N * (uint32_t)dd;
-  const uint64_t q_head = ((uint64_t)wc.b * H_Q + wc.h) * head_elems;
-  const uint64_t kv_head = ((uint64_t)wc.b * H_KV + kvh) * head_elems;
-  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(q + q_head, head_elems * 2);
-  const __amdgpu_buffer_rsrc_t o_rs = make_rsrc(o + q_head, head_elems * 2);
-  const u32x4 k_desc = make_desc(k + kv_head, head_elems * 2);
-  const u32x4 v_desc = make_desc(v + kv_head, head_elems * 2);
+  const uint32_t q_elems = (uint32_t)N_q * (uint32_t)dd;
+  const uint32_t kv_elems = (uint32_t)N_kv * (uint32_t)dd;
+  const uint64_t q_head = ((uint64_t)wc.b * H_Q + wc.h) * q_elems;
+  const uint64_t kv_head = ((uint64_t)wc.b * H_KV + kvh) * kv_elems;
+  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(q + q_head, q_elems * 2);
+  const __amdgpu_buffer_rsrc_t o_rs = make_rsrc(o + q_head, q_elems * 2);
+  const u32x4 k_desc = make_desc(k + kv_head, kv_elems * 2);
+  const u32x4 v_desc = make_desc(v + kv_head, kv_elems * 2);
 
   // ---- Q fragments: B operand of S^T = K Q^T; for query block qb the lane
   // holds Q[row][16kc+8g..+7] of row 64 wave + 32 qb + l32.
   const int wave_row_first = row0 + wave * 64;
   const int wave_row_last = wave_row_first + 63;
   int my_row[kQB];
+  int my_last_key[kQB];  // causal: last key the row sees
   bf16x8 qf[kQB][C::KC];
   static_for<kQB>([&](auto qbi) {
     constexpr int qb = decltype(qbi)::value;
     my_row[qb] = wave_row_first + qb * 32 + l32;
+    my_last_key[qb] = my_row[qb] + off;
     static_for<C::KC>([&](auto kci) {
       constexpr int kc = decltype(kci)::value;
       const int col = kc * 16 + g * 8;
@@ -372,7 +388,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   });
   constexpr bool kPairs = FULL_D && C::LOADS % 2 == 0;
   const uint32_t tile_bytes = (uint32_t)kBlockN * (uint32_t)dd * 2u;
-  const int32_t head_bytes = (int32_t)(head_elems * 2u);
+  const int32_t head_bytes = (int32_t)(kv_elems * 2u);
+  const int tile0 = kv_begin / kBlockN;  // first tile of the key range
   const uint32_t lds_base = (uint32_t)(uintptr_t)(
       (__attribute__((address_space(3))) char*)lds_b);
   const uint32_t m0_wave = lds_base + (uint32_t)wave_blk0 * 1024u;
@@ -381,7 +398,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // Byte offset of a tile, capped at the head size: a tile past the end then
   // reads nothing, and soff + kOutOfRange stays below 2^32.
   auto tile_soff = [&](int tile) {
-    const uint32_t soff = (uint32_t)tile * tile_bytes;
+    const uint32_t soff = (uint32_t)(tile0 + tile) * tile_bytes;
     return soff < (uint32_t)head_bytes ? soff : (uint32_t)head_bytes;
   };
   // All loads of one tile of one operand, into LDS buffer `lds_byte`.
@@ -523,27 +540,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + (r >> 2) * 8 + g * 4 + (r & 3);
-        const bool ok = key < N && (!CAUSAL || key <= my_row[qb]);
+        const bool ok = key < kv_end && (!CAUSAL || key <= my_last_key[qb]);
         s[qb][r] = ok ? s[qb][r] : -INFINITY;
       }
     });
   };
 
-  // ---- tiles
-  const int n_tiles_all = (N + kBlockN - 1) / kBlockN;
-  int n_tiles = n_tiles_all;
-  if (CAUSAL) {
-    const int last = (row0 + kBlockM + kBlockN - 1) / kBlockN;
-    n_tiles = last < n_tiles_all ? last : n_tiles_all;
-  }
+  // ---- tiles j = 0, 1, ... of the key range: keys kv_begin + 32 j ..
+  // Keys some row of the workgroup sees end at span_end.
+  int span_end = kv_end;
+  if (CAUSAL) span_end = min(span_end, row0 + kBlockM + off);
+  const int n_tiles = span_end > kv_begin ? (span_end - kv_begin + kBlockN - 1) / kBlockN : 0;
   // Steady tiles need no mask for any row of the workgroup and have a
-  // successor: keys of tile j all < N and (causal) <= the block's first row.
-  int n_steady = N / kBlockN;
+  // successor: keys of tile j all < kv_end and (causal) seen by the block's
+  // first row.
+  int n_steady = (kv_end - kv_begin) / kBlockN;
   if (CAUSAL) {
-    const int full = (row0 + 1) / kBlockN;
-    n_steady = full < n_steady ? full : n_steady;
+    const int x = row0 + off + 1 - kv_begin;
+    n_steady = min(n_steady, x > 0 ? x / kBlockN : 0);
   }
-  if (n_steady > n_tiles - 1) n_steady = n_tiles - 1;
+  n_steady = min(n_steady, n_tiles - 1);
+
+  // A workgroup none of whose rows sees a key of its range computes nothing:
+  // its rows get O = 0 and lse = -inf.
+  if (n_tiles > 0) {
 
   // ---- prologue: zero LDS (slots no load writes must read as zero), then
   // fill the pipeline.  Tile t's K lives in K buffer t % 4 and its V in V
@@ -737,13 +757,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   float mx_t[kQB];
   for (;;) {
   for (; j < n_tiles; ++j) {
-    const int key0 = j * kBlockN;
-    // A wave whose last row precedes a tile has nothing to do for it.
-    const bool act_cur = !CAUSAL || key0 <= wave_row_last;
+    const int key0 = kv_begin + j * kBlockN;
+    // A wave none of whose rows sees a key of a tile has nothing to do for it.
+    const bool act_cur = !CAUSAL || key0 <= wave_row_last + off;
     bool raise = false;
     if (act_cur) {
-      if ((key0 + kBlockN > N) ||
-          (CAUSAL && key0 + kBlockN - 1 > wave_row_first))
+      if ((key0 + kBlockN > kv_end) ||
+          (CAUSAL && key0 + kBlockN - 1 > wave_row_first + off))
         mask(s_cur, key0);
       static_for<kQB>([&](auto qbi) {
         constexpr int qb = decltype(qbi)::value;
@@ -754,7 +774,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     if (raise) break;
     if (j + kStages < n_tiles) load_k(j + kStages);
     if (j + kStages - 1 < n_tiles) load_v(j + kStages - 1);
-    const bool act_next = j + 1 < n_tiles && (!CAUSAL || key0 + kBlockN <= wave_row_last);
+    const bool act_next = j + 1 < n_tiles && (!CAUSAL || key0 + kBlockN <= wave_row_last + off);
     // act_next implies act_cur, so this tile's softmax and P V MFMAs always
     // separate these score MFMAs from the next iteration's reads of them.
     f32x16 s_next[kQB];
@@ -777,15 +797,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     raise_max(qb, mx_t[qb]);
   });
   }
+  }  // n_tiles > 0
 
-  // ---- epilogue: O /= l, lse = ln2 (m + log2 l)
+  // ---- epilogue: O /= l, lse = ln2 (m + log2 l); a row that saw no key
+  // (l = 0) gets O = 0 and lse = -inf.  With one split O goes to o as bf16
+  // and lse to lse; with several, the split's normalised O goes to o_ws as
+  // fp32 [split][b][h][row][d] and its lse to lse_ws [split][b][h][row].
   static_for<kQB>([&](auto qbi) {
     static_for<C::DB>([&](auto dbi) { xdl_guard_a(oacc[decltype(qbi)::value][decltype(dbi)::value]); });
   });
+  const bool partial = o_ws != nullptr;
+  const uint64_t part_rows =
+      (((uint64_t)split * B + wc.b) * H_Q + wc.h) * (uint64_t)N_q;  // first row of the head
   static_for<kQB>([&](auto qbi) {
     constexpr int qb = decltype(qbi)::value;
     const float l_tot = xhalf_sum(l_run[qb]);
-    const float inv = 1.f / l_tot;
+    const bool seen = l_tot > 0.f;
+    const float inv = seen ? 1.f / l_tot : 0.f;
+    const bool row_ok = my_row[qb] < N_q;
     // O^T accumulator r of block db is dim 32db + 8(r/4) + 4g + (r%4).
     static_for<C::DB>([&](auto dbi) {
       constexpr int db = decltype(dbi)::value;
@@ -793,18 +822,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       for (int rr = 0; rr < 4; ++rr) {
         const int col = db * 32 + rr * 8 + g * 4;
         if (FULL_D || col < dd) {
-          u32x2 w;
-          w.x = pack_bf16x2(oacc[qb][db][rr * 4 + 0] * inv, oacc[qb][db][rr * 4 + 1] * inv);
-          w.y = pack_bf16x2(oacc[qb][db][rr * 4 + 2] * inv, oacc[qb][db][rr * 4 + 3] * inv);
-          __builtin_amdgcn_raw_buffer_store_b64(
-              w, o_rs, (uint32_t)(my_row[qb] * dd + col) * 2u, 0, 0);
+          const float o0 = oacc[qb][db][rr * 4 + 0] * inv, o1 = oacc[qb][db][rr * 4 + 1] * inv;
+          const float o2 = oacc[qb][db][rr * 4 + 2] * inv, o3 = oacc[qb][db][rr * 4 + 3] * inv;
+          if (!partial) {
+            u32x2 w;
+            w.x = pack_bf16x2(o0, o1);
+            w.y = pack_bf16x2(o2, o3);
+            __builtin_amdgcn_raw_buffer_store_b64(
+                w, o_rs, (uint32_t)(my_row[qb] * dd + col) * 2u, 0, 0);
+          } else if (row_ok) {
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<f32x4*>(o_ws + (part_rows + my_row[qb]) * (uint64_t)d + col) =
+                f32x4{o0, o1, o2, o3};
+          }
         }
       }
     });
-    if (lse != nullptr && g == 0 && my_row[qb] < N) {
+    if (g == 0 && row_ok) {
       const float ln2 = 0.6931471805599453f;
-      lse[((uint64_t)wc.b * H_Q + wc.h) * (uint64_t)N + my_row[qb]] =
-          (m_run[qb] + __builtin_amdgcn_logf(l_tot)) * ln2;
+      const float lse_row = seen ? (m_run[qb] + __builtin_amdgcn_logf(l_tot)) * ln2 : -INFINITY;
+      if (partial)
+        lse_ws[part_rows + my_row[qb]] = lse_row;
+      else if (lse != nullptr)
+        lse[((uint64_t)wc.b * H_Q + wc.h) * (uint64_t)N_q + my_row[qb]] = lse_row;
     }
   });
 }

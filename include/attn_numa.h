@@ -82,6 +82,68 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              void* stream);
 
 /*
+ * attn_fwd_split: attention of N_q query rows over N_kv keys, optionally with
+ * the keys split into num_splits ranges computed by separate workgroups and
+ * merged (split-KV, e.g. decode with N_q = 1).
+ *
+ * Passage: the per-head attention of attn_fwd (digest page §4 equation, §3
+ * Figure 4); the split and merge are the decode reduction of the "Fused
+ * Grouped-Query Attention" page (each shard computes attention over its KV
+ * range; the partial results are reduced into the output), in (O, lse) form:
+ * lse = ln sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s.
+ *
+ *   q, o   device, bf16 [B][H_Q][N_q][d];  k, v  device, bf16 [B][H_KV][N_kv][d]
+ *   lse    device, fp32 [B][H_Q][N_q] or NULL
+ *   causal 1: bottom-right aligned, query row i sees keys 0 .. i + N_kv - N_q
+ *          (the attn_fwd mask when N_q == N_kv; every key when N_q == 1).
+ *          A row that sees no key gets O = 0 and lse = -inf.
+ *   num_splits >= 1.  Split s covers keys [s c, min((s+1) c, N_kv)) with
+ *          c = attn_split_chunk(N_kv, num_splits); a split past the keys is
+ *          empty.  With num_splits == 1 the result goes straight to o and lse
+ *          and o_ws, lse_ws are ignored (may be NULL); then the call equals
+ *          attn_fwd when N_q == N_kv (bit-identical).
+ *   o_ws   device, fp32 [num_splits][B][H_Q][N_q][d], caller-owned workspace:
+ *          split s's output normalised over its keys (0 for rows that see
+ *          none of them).  Used when num_splits > 1.
+ *   lse_ws device, fp32 [num_splits][B][H_Q][N_q]: split s's natural-log
+ *          logsumexp (-inf for rows that see none of its keys).
+ *   Other arguments and limits as attn_fwd (N_q and N_kv each obey N's
+ *   limits; B*H_Q*ceil(N_q/256)*num_splits < 2^31).
+ * Launches the attention kernel, then (num_splits > 1) the merge kernel, on
+ * `stream`.  Errors: as attn_fwd; ATTN_E_NULL also for a NULL workspace with
+ * num_splits > 1, ATTN_E_ALIGN for a misaligned one.
+ */
+int attn_fwd_split(const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int H_Q, int H_KV, int N_q, int N_kv,
+                   int d, int causal, int num_splits, float* o_ws,
+                   float* lse_ws, int mapping, void* stream);
+
+/*
+ * attn_split_chunk: keys per split for attn_fwd_split, ceil(N_kv /
+ * num_splits) rounded up to a multiple of 32 (whole key tiles).  Needs no
+ * GPU.  Errors: ATTN_E_SHAPE for N_kv <= 0 or num_splits < 1.
+ */
+int attn_split_chunk(int N_kv, int num_splits);
+
+/*
+ * attn_merge: merge num_splits partial results into one (the same reduction
+ * as attn_fwd_split; also usable for partial results computed elsewhere,
+ * e.g. per device).
+ *
+ *   o_parts   device, fp32 [num_splits][B][H_Q][N_q][d], read only
+ *   lse_parts device, fp32 [num_splits][B][H_Q][N_q] (natural log; -inf for
+ *             a part with no keys), read only
+ *   o         device, bf16 [B][H_Q][N_q][d], written
+ *   lse       device, fp32 [B][H_Q][N_q], written, may be NULL
+ * A row whose parts are all -inf gets O = 0 and lse = -inf.
+ * Errors: ATTN_E_NULL, ATTN_E_SHAPE, ATTN_E_HEAD_DIM, ATTN_E_ALIGN,
+ * ATTN_E_NO_DEVICE, ATTN_E_HIP.
+ */
+int attn_merge(const float* o_parts, const float* lse_parts, int num_splits,
+               int B, int H_Q, int N_q, int d, void* o, float* lse,
+               void* stream);
+
+/*
  * attn_wg_map: the remap table the kernel uses, computed on the host.
  *
  * Passage: digest page §2 Q1 (dispatch to XCD w mod X), §2 Q2 and §7

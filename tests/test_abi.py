@@ -34,7 +34,8 @@ def _declared_codes():
 
 def test_library_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert set(names) == {"attn_fwd", "attn_wg_map", "attn_num_xcd", "attn_block_m",
+    assert set(names) == {"attn_fwd", "attn_fwd_split", "attn_split_chunk", "attn_merge",
+                          "attn_wg_map", "attn_num_xcd", "attn_block_m",
                           "attn_probe_placement", "attn_strerror"}
     for n in names:
         assert hasattr(lib, n), n
@@ -155,3 +156,46 @@ def test_num_xcd_env_override(monkeypatch):
     if torch.cuda.is_available():
         pytest.skip("covered by the GPU placement test")
     assert lib.attn_num_xcd() == _declared_codes()["ATTN_E_NO_DEVICE"]
+
+
+def test_split_chunk_rule(lib):
+    """ceil(N_kv / S) rounded up to whole 32-key tiles; the splits cover the
+    keys exactly once."""
+    c = _declared_codes()
+    for N_kv, S in [(1, 1), (31, 1), (32, 2), (100, 4), (40, 4), (131072, 64), (1000, 7)]:
+        chunk = attn.attn_split_chunk(N_kv, S)
+        assert chunk % 32 == 0 and chunk >= -(-N_kv // S)
+        assert chunk < -(-N_kv // S) + 32
+        covered = sum(max(0, min((s + 1) * chunk, N_kv) - s * chunk) for s in range(S))
+        assert covered == N_kv
+    assert lib.attn_split_chunk(0, 1) == c["ATTN_E_SHAPE"]
+    assert lib.attn_split_chunk(10, 0) == c["ATTN_E_SHAPE"]
+
+
+def _split(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, H_Q=8, H_KV=8, N_q=16,
+           N_kv=1024, d=128, causal=0, S=4, o_ws=FAKE, lse_ws=FAKE, mapping=3):
+    return lib.attn_fwd_split(q, k, v, o, lse, B, H_Q, H_KV, N_q, N_kv, d, causal, S,
+                              o_ws, lse_ws, mapping, None)
+
+
+def test_split_and_merge_argument_errors(lib):
+    """Rejected before anything could launch on the fake pointers."""
+    c = _declared_codes()
+    assert _split(lib, q=None) == c["ATTN_E_NULL"]
+    assert _split(lib, o_ws=None) == c["ATTN_E_NULL"]
+    assert _split(lib, lse_ws=None) == c["ATTN_E_NULL"]
+    for kw in ({"N_q": 0}, {"N_kv": 0}, {"S": 0}, {"H_Q": 6, "H_KV": 4},
+               {"B": 1 << 12, "H_Q": 1 << 10, "N_q": 256, "S": 1 << 10}):
+        assert _split(lib, **kw) == c["ATTN_E_SHAPE"], kw
+    assert _split(lib, d=12) == c["ATTN_E_HEAD_DIM"]
+    assert _split(lib, mapping=4) == c["ATTN_E_MAPPING"]
+    assert _split(lib, o_ws=FAKE + 4) == c["ATTN_E_ALIGN"]
+    m = lambda **kw: lib.attn_merge(kw.get("op", FAKE), kw.get("lp", FAKE), kw.get("S", 2),
+                                    kw.get("B", 1), kw.get("H", 2), kw.get("N", 3),
+                                    kw.get("d", 64), kw.get("o", FAKE), kw.get("lse", None), None)
+    assert m(op=None) == c["ATTN_E_NULL"]
+    assert m(o=None) == c["ATTN_E_NULL"]
+    assert m(S=0) == c["ATTN_E_SHAPE"]
+    assert m(N=0) == c["ATTN_E_SHAPE"]
+    assert m(d=7) == c["ATTN_E_HEAD_DIM"]
+    assert m(lp=FAKE + 8) == c["ATTN_E_ALIGN"]
