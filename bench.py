@@ -63,6 +63,24 @@ SWEEP = ["mha_h8_1k", "mha_8k", "mha_8k_causal", "mha_32k", "mha_32k_causal",
          "mha12_b1_32k_causal", "dsv3_d56_32k_causal", "dsv3_d56_128k_causal"]
 
 
+# Split-KV (decode) configurations: (B, H_Q, H_KV, N_q, N_kv, d, causal,
+# splits).  Decode streams each KV head once, so HBM bandwidth bounds it.
+SPLIT_WORKLOADS = {
+    "decode_gqa64x8_b16_128k": (16, 64, 8, 1, 131072, 128, True, 16),
+    "decode_gqa64x8_b64_32k": (64, 64, 8, 1, 32768, 128, True, 8),
+    "decode_mha32_b8_32k": (8, 32, 32, 1, 32768, 128, True, 16),
+}
+HBM_PEAK_GBS = 8000.0
+
+
+def split_bytes(B, H_Q, H_KV, N_q, N_kv, d, S) -> float:
+    """Unique bytes of one call: Q, K, V, O (bf16), lse, and the fp32
+    partials written and read back when S > 1."""
+    rows = B * H_Q * N_q
+    ws = 2 * S * rows * (d + 1) * 4 if S > 1 else 0
+    return 2.0 * (2 * rows * d + 2 * B * H_KV * N_kv * d) + 4 * rows + ws
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -361,10 +379,57 @@ def run_sweep(out_path: str):
         t = [res[m] for m in MODE_NAMES]
         lines.append(f"| {describe(name)} | {flops / 1e12:.2f} | {t[0]:.0f} | {t[1]:.0f} | {t[2]:.0f} | "
                      f"{t[3]:.0f} ({100 * t[3] / PEAK_BF16_TFLOPS:.1f}%) | {t[3] / t[0]:.2f} |")
-    lines += ["", f"Command: `python3 bench.py --sweep {out_path}`"]
+    split_rows = []
+    for name, (B, H_Q, H_KV, N_q, N_kv, d, causal, S) in SPLIT_WORKLOADS.items():
+        q = inputs.normal_bf16((B, H_Q, N_q, d), 1000, "cuda")
+        k = inputs.normal_bf16((B, H_KV, N_kv, d), 1001, "cuda")
+        v = inputs.normal_bf16((B, H_KV, N_kv, d), 1002, "cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty(B, H_Q, N_q, device="cuda", dtype=torch.float32)
+        o_ws = torch.empty(S, B, H_Q, N_q, d, device="cuda", dtype=torch.float32)
+        lse_ws = torch.empty(S, B, H_Q, N_q, device="cuda", dtype=torch.float32)
+        flops = 4.0 * B * H_Q * d * N_q * N_kv
+        nbytes = split_bytes(B, H_Q, H_KV, N_q, N_kv, d, S)
+        stream = torch.cuda.current_stream()
+        res = {}
+        for mode in (0, 3):
+            for _ in range(2):
+                attn.attn_fwd_split(q, k, v, causal=causal, num_splits=S, mapping=mode, o=o,
+                                    lse=lse, o_ws=o_ws, lse_ws=lse_ws, stream=stream)
+            ts = []
+            for _ in range(10):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                attn.attn_fwd_split(q, k, v, causal=causal, num_splits=S, mapping=mode, o=o,
+                                    lse=lse, o_ws=o_ws, lse_ws=lse_ws, stream=stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ms = sorted(ts)[len(ts) // 2]
+            res[MODE_NAMES[mode]] = {"ms": ms, "gbs": nbytes / (ms / 1e3) / 1e9,
+                                     "tflops": flops / (ms / 1e3) / 1e12}
+            log(f"  {name:24s} {MODE_NAMES[mode]:22s} {ms:9.3f} ms "
+                f"{res[MODE_NAMES[mode]]['gbs']:8.0f} GB/s")
+        split_rows.append((name, (B, H_Q, H_KV, N_q, N_kv, d, causal, S), nbytes, res))
+        del q, k, v, o, lse, o_ws, lse_ws
+        torch.cuda.empty_cache()
+    lines += ["", "## Split-KV decode (attn_fwd_split + merge, one call)", "",
+              "HBM-bound: bytes = Q + K + V + O + lse + the fp32 partials written and read back; "
+              f"GB/s against the {HBM_PEAK_GBS:.0f} GB/s HBM peak. Median of 10 calls.", "",
+              "| configuration | splits | MB | NBF ms | SHF ms | SHF GB/s (% of peak) |",
+              "|---|---|---|---|---|---|"]
+    for name, (B, H_Q, H_KV, N_q, N_kv, d, causal, S), nbytes, res in split_rows:
+        sh = res["swizzled_head_first"]
+        lines.append(f"| decode B={B} H_Q={H_Q} H_KV={H_KV} N_q={N_q} N_kv={N_kv} d={d} "
+                     f"{'causal' if causal else ''} | {S} | {nbytes / 1e6:.0f} | "
+                     f"{res['naive_block_first']['ms']:.3f} | {sh['ms']:.3f} | "
+                     f"{sh['gbs']:.0f} ({100 * sh['gbs'] / HBM_PEAK_GBS:.1f}%) |")
+    lines += ["", "Command: `python3 bench.py --sweep OUT.md` (this file is OUT.md)."]
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
-    print(json.dumps({"sweep": {name: res for name, _, res in rows}}))
+    print(json.dumps({"sweep": {name: res for name, _, res in rows},
+                      "split": {name: res for name, _, _, res in split_rows}}))
 
 
 def main():

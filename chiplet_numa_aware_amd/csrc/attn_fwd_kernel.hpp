@@ -302,8 +302,8 @@ template <int D, bool CAUSAL, bool FULL_D>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int B, int H_Q, int H_KV, int N_q, int N_kv, int d,
-    int M_q, int kv_chunk, int num_splits, float* __restrict__ o_ws,
+    float* __restrict__ lse, int B, int H_U, int H_KV, int N_rows, int pos_mod,
+    int N_kv, int d, int M_q, int kv_chunk, int num_splits, float* __restrict__ o_ws,
     float* __restrict__ lse_ws, int mapping, int num_xcd, float scale_log2) {
   using C = TileCfg<D>;
   using TS = TileSchedule<D>;
@@ -318,24 +318,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   const int g = lane >> 5;     // lane half: which 8 of 16 MFMA k values
   const int l32 = lane & 31;   // query row within a query block / MFMA column
 
-  // The remap sees M_q * num_splits row blocks per head: m' = split * M_q +
+  // Rows are grouped in units of N_rows consecutive rows of q, o and lse: a
+  // query head (H_U = H_Q, N_rows = N_q), or the G query heads of one KV group
+  // (H_U = H_KV, N_rows = G N_q: the heads are contiguous in [B][H_Q][N_q][d]),
+  // which fills the rows of a workgroup when N_q is small (decode).  Row r of
+  // a unit is at causal position r mod pos_mod (pos_mod = N_q).
+  // The remap sees M_q * num_splits row blocks per unit: m' = split * M_q +
   // row block, so the workgroups of one key range are adjacent.
-  const WgCoord wc = wg_map(mapping, blockIdx.x, B, H_Q, M_q * num_splits, num_xcd);
-  const int kvh = (int)wc.h / (H_Q / H_KV);
+  const WgCoord wc = wg_map(mapping, blockIdx.x, B, H_U, M_q * num_splits, num_xcd);
+  const int kvh = (int)wc.h / (H_U / H_KV);
   const int split = (int)wc.m / M_q;
   const int row0 = ((int)wc.m - split * M_q) * kBlockM;
   // Keys of this workgroup: [kv_begin, kv_end), tile-aligned.  Causal: query
   // row r sees keys <= r + off (bottom-right aligned; off = 0 when N_q == N_kv).
   const int kv_begin = split * kv_chunk;
   const int kv_end = min(kv_begin + kv_chunk, N_kv);
-  const int off = CAUSAL ? N_kv - N_q : 0;
+  const int off = CAUSAL ? N_kv - pos_mod : 0;
 
   // Row length in elements: the compile-time D when d == D, so that every
   // per-lane offset below is a constant multiple and folds into immediates.
   const int dd = FULL_D ? D : d;
-  const uint32_t q_elems = (uint32_t)N_q * (uint32_t)dd;
+  const uint32_t q_elems = (uint32_t)N_rows * (uint32_t)dd;
   const uint32_t kv_elems = (uint32_t)N_kv * (uint32_t)dd;
-  const uint64_t q_head = ((uint64_t)wc.b * H_Q + wc.h) * q_elems;
+  const uint64_t q_head = ((uint64_t)wc.b * H_U + wc.h) * q_elems;
   const uint64_t kv_head = ((uint64_t)wc.b * H_KV + kvh) * kv_elems;
   const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(q + q_head, q_elems * 2);
   const __amdgpu_buffer_rsrc_t o_rs = make_rsrc(o + q_head, q_elems * 2);
@@ -345,14 +350,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // ---- Q fragments: B operand of S^T = K Q^T; for query block qb the lane
   // holds Q[row][16kc+8g..+7] of row 64 wave + 32 qb + l32.
   const int wave_row_first = row0 + wave * 64;
-  const int wave_row_last = wave_row_first + 63;
+  // Causal positions spanned by the valid rows (< N_rows) of rows [r0, r1]:
+  // exact when the rows lie in one unit, else the whole range 0 .. pos_mod-1.
+  auto pos_range = [&](int r0, int r1, int& pmin, int& pmax) {
+    r1 = min(r1, N_rows - 1);
+    if (r0 / pos_mod == r1 / pos_mod) {
+      pmin = r0 % pos_mod;
+      pmax = r1 % pos_mod;
+    } else {
+      pmin = 0;
+      pmax = pos_mod - 1;
+    }
+  };
+  // A wave with no valid row only loads its share of the K/V tiles.
+  const bool wave_idle = wave_row_first >= N_rows;
+  int wave_pmin = 0, wave_pmax = 0, wg_pmin = 0, wg_pmax = 0;
+  if (!wave_idle) pos_range(wave_row_first, wave_row_first + 63, wave_pmin, wave_pmax);
+  pos_range(row0, row0 + kBlockM - 1, wg_pmin, wg_pmax);
   int my_row[kQB];
   int my_last_key[kQB];  // causal: last key the row sees
   bf16x8 qf[kQB][C::KC];
   static_for<kQB>([&](auto qbi) {
     constexpr int qb = decltype(qbi)::value;
     my_row[qb] = wave_row_first + qb * 32 + l32;
-    my_last_key[qb] = my_row[qb] + off;
+    my_last_key[qb] = my_row[qb] % pos_mod + off;
     static_for<C::KC>([&](auto kci) {
       constexpr int kc = decltype(kci)::value;
       const int col = kc * 16 + g * 8;
@@ -549,14 +570,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // ---- tiles j = 0, 1, ... of the key range: keys kv_begin + 32 j ..
   // Keys some row of the workgroup sees end at span_end.
   int span_end = kv_end;
-  if (CAUSAL) span_end = min(span_end, row0 + kBlockM + off);
+  if (CAUSAL) span_end = min(span_end, wg_pmax + 1 + off);
   const int n_tiles = span_end > kv_begin ? (span_end - kv_begin + kBlockN - 1) / kBlockN : 0;
   // Steady tiles need no mask for any row of the workgroup and have a
   // successor: keys of tile j all < kv_end and (causal) seen by the block's
   // first row.
   int n_steady = (kv_end - kv_begin) / kBlockN;
   if (CAUSAL) {
-    const int x = row0 + off + 1 - kv_begin;
+    const int x = wg_pmin + off + 1 - kv_begin;
     n_steady = min(n_steady, x > 0 ? x / kBlockN : 0);
   }
   n_steady = min(n_steady, n_tiles - 1);
@@ -586,6 +607,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   scores(k_buf(0), sb[0]);
   xdl_guard_v(sb[0][0], sb[0][1]);
 
+  if (wave_idle) {
+    // No valid rows: only this wave's share of every tile load, with one
+    // barrier per tile like the computing waves, and the same two tiles of
+    // loads in flight at each barrier (tiles past the end read nothing).
+    for (int jj = 0; jj < n_tiles; ++jj) {
+      load_k(jj + kStages);
+      load_v(jj + kStages - 1);
+      wait_vmcnt<2 * 2 * C::LOADS>();
+      barrier();
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  } else {
   int j = 0;
   // Steady state: per tile, one basic block of TS::T MFMA bundles; the row
   // max of S_{j+1} is taken under the P V MFMAs.  A tile's loads must land
@@ -759,11 +792,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   for (; j < n_tiles; ++j) {
     const int key0 = kv_begin + j * kBlockN;
     // A wave none of whose rows sees a key of a tile has nothing to do for it.
-    const bool act_cur = !CAUSAL || key0 <= wave_row_last + off;
+    const bool act_cur = !wave_idle && (!CAUSAL || key0 <= wave_pmax + off);
     bool raise = false;
     if (act_cur) {
       if ((key0 + kBlockN > kv_end) ||
-          (CAUSAL && key0 + kBlockN - 1 > wave_row_first + off))
+          (CAUSAL && key0 + kBlockN - 1 > wave_pmin + off))
         mask(s_cur, key0);
       static_for<kQB>([&](auto qbi) {
         constexpr int qb = decltype(qbi)::value;
@@ -774,7 +807,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     if (raise) break;
     if (j + kStages < n_tiles) load_k(j + kStages);
     if (j + kStages - 1 < n_tiles) load_v(j + kStages - 1);
-    const bool act_next = j + 1 < n_tiles && (!CAUSAL || key0 + kBlockN <= wave_row_last + off);
+    const bool act_next = !wave_idle && j + 1 < n_tiles && (!CAUSAL || key0 + kBlockN <= wave_pmax + off);
     // act_next implies act_cur, so this tile's softmax and P V MFMAs always
     // separate these score MFMAs from the next iteration's reads of them.
     f32x16 s_next[kQB];
@@ -797,6 +830,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     raise_max(qb, mx_t[qb]);
   });
   }
+  }  // !wave_idle
   }  // n_tiles > 0
 
   // ---- epilogue: O /= l, lse = ln2 (m + log2 l); a row that saw no key
@@ -808,13 +842,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   });
   const bool partial = o_ws != nullptr;
   const uint64_t part_rows =
-      (((uint64_t)split * B + wc.b) * H_Q + wc.h) * (uint64_t)N_q;  // first row of the head
+      (((uint64_t)split * B + wc.b) * H_U + wc.h) * (uint64_t)N_rows;  // first row of the unit
   static_for<kQB>([&](auto qbi) {
     constexpr int qb = decltype(qbi)::value;
     const float l_tot = xhalf_sum(l_run[qb]);
     const bool seen = l_tot > 0.f;
     const float inv = seen ? 1.f / l_tot : 0.f;
-    const bool row_ok = my_row[qb] < N_q;
+    const bool row_ok = my_row[qb] < N_rows;
     // O^T accumulator r of block db is dim 32db + 8(r/4) + 4g + (r%4).
     static_for<C::DB>([&](auto dbi) {
       constexpr int db = decltype(dbi)::value;
@@ -844,7 +878,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       if (partial)
         lse_ws[part_rows + my_row[qb]] = lse_row;
       else if (lse != nullptr)
-        lse[((uint64_t)wc.b * H_Q + wc.h) * (uint64_t)N_q + my_row[qb]] = lse_row;
+        lse[((uint64_t)wc.b * H_U + wc.h) * (uint64_t)N_rows + my_row[qb]] = lse_row;
     }
   });
 }

@@ -104,7 +104,7 @@ struct FwdArgs {
   const void *q, *k, *v;
   void* o;
   float* lse;
-  int B, H_Q, H_KV, N_q, N_kv, d, M_q, kv_chunk, num_splits;
+  int B, H_U, H_KV, N_rows, pos_mod, N_kv, d, M_q, kv_chunk, num_splits;
   float *o_ws, *lse_ws;
   int W, mapping, X;
   float scale_log2;
@@ -116,7 +116,7 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
                      stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o),
-                     a.lse, a.B, a.H_Q, a.H_KV, a.N_q, a.N_kv, a.d, a.M_q, a.kv_chunk,
+                     a.lse, a.B, a.H_U, a.H_KV, a.N_rows, a.pos_mod, a.N_kv, a.d, a.M_q, a.kv_chunk,
                      a.num_splits, a.o_ws, a.lse_ws, a.mapping, a.X, a.scale_log2);
   return hipGetLastError();
 }
@@ -137,9 +137,12 @@ int64_t split_chunk(int N_kv, int S) {
   return (per + kBlockN - 1) / kBlockN * kBlockN;
 }
 
+// pack: group the G = H_Q / H_KV query heads of each KV group into one unit
+// of G * N_q rows (see the kernel); used by attn_fwd_split for short N_q.
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H_Q, int H_KV, int N_q, int N_kv, int d, int causal,
-             int num_splits, float* o_ws, float* lse_ws, int mapping, void* stream) {
+             int num_splits, float* o_ws, float* lse_ws, int mapping, bool pack,
+             void* stream) {
   if (!q || !k || !v || !o) return ATTN_E_NULL;
   if (N_q <= 0 || N_kv <= 0 || num_splits < 1) return ATTN_E_SHAPE;
   int M = 0, W = 0;
@@ -158,10 +161,15 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   int X = 1;
   rc = resolve_xcd(&X);
   if (rc != ATTN_OK) return rc;
-  FwdArgs a{q, k, v, o, lse, B, H_Q, H_KV, N_q, N_kv, d, M,
+  const int G = H_Q / H_KV;
+  pack = pack && G > 1 && (int64_t)G * N_q * d * 2 <= kMaxHeadBytes;
+  const int H_U = pack ? H_KV : H_Q;
+  const int N_rows = pack ? G * N_q : N_q;  // <= kBlockM * G when packing
+  const int M_q = (N_rows + kBlockM - 1) / kBlockM;
+  FwdArgs a{q, k, v, o, lse, B, H_U, H_KV, N_rows, N_q, N_kv, d, M_q,
             (int)split_chunk(N_kv, num_splits), num_splits,
             num_splits > 1 ? o_ws : nullptr, num_splits > 1 ? lse_ws : nullptr,
-            W * num_splits, mapping, X,
+            B * H_U * M_q * num_splits, mapping, X,
             (float)(1.4426950408889634 / std::sqrt((double)d))};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = (d <= 64) ? launch<64>(a, causal, s) : launch<128>(a, causal, s);
@@ -203,7 +211,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H_Q, int H_KV, int N, int d, int causal, int mapping,
              void* stream) {
   return fwd_impl(q, k, v, o, lse, B, H_Q, H_KV, N, N, d, causal, 1, nullptr,
-                  nullptr, mapping, stream);
+                  nullptr, mapping, false, stream);
 }
 
 int attn_fwd_split(const void* q, const void* k, const void* v, void* o,
@@ -211,7 +219,7 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o,
                    int d, int causal, int num_splits, float* o_ws,
                    float* lse_ws, int mapping, void* stream) {
   return fwd_impl(q, k, v, o, lse, B, H_Q, H_KV, N_q, N_kv, d, causal,
-                  num_splits, o_ws, lse_ws, mapping, stream);
+                  num_splits, o_ws, lse_ws, mapping, N_q < kBlockM, stream);
 }
 
 int attn_split_chunk(int N_kv, int num_splits) {

@@ -55,8 +55,13 @@ SPLIT_CASES = [
     (1, 2, 1, 513, 777, 56, True, 4),
     (1, 2, 2, 40, 40, 128, False, 4),       # chunk 32: splits 2 and 3 are empty
     (1, 2, 2, 200, 100, 128, True, 2),      # N_q > N_kv: early rows see no key
-    (2, 8, 2, 1, 3000, 128, True, 8),       # decode, GQA
+    (2, 8, 2, 1, 3000, 128, True, 8),       # decode, GQA (packed: 4 heads per unit)
     (1, 4, 4, 7, 4096, 64, True, 16),
+    # GQA with N_q < 256: the heads of a KV group share the rows of a workgroup
+    (1, 8, 2, 37, 1000, 128, True, 3),      # units of 148 rows
+    (2, 16, 2, 100, 700, 64, True, 2),      # units of 800 rows: heads wrap inside blocks
+    (1, 8, 1, 255, 255, 128, True, 1),      # one unit of 2040 rows, N_q == N_kv
+    (1, 6, 3, 90, 2500, 56, False, 5),
 ]
 
 
@@ -93,8 +98,9 @@ def test_single_split_equals_attn_fwd_bitwise(causal):
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_split_bitwise_identical_across_mappings():
-    q, k, v = _qkv(2, 8, 4, 300, 2000, 128, seed=78)
+@pytest.mark.parametrize("N_q", [300, 60])   # 60: packed rows
+def test_split_bitwise_identical_across_mappings(N_q):
+    q, k, v = _qkv(2, 8, 4, N_q, 2000, 128, seed=78)
     ref = None
     for mapping in range(4):
         o, l = attn.attn_fwd_split(q, k, v, causal=True, num_splits=6, mapping=mapping)
@@ -132,3 +138,17 @@ def test_merge_kernel_matches_oracle():
     assert_close(f64(o)[fin], f64(lse)[fin], o_ref[fin], lse_ref[fin], what="merge")
     assert np.all(f64(o)[~fin] == 0)
     _check_lse_inf_pattern(f64(lse), lse_ref, "merge lse")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_rows_agree_with_attn_fwd(causal):
+    """N_q == N_kv < 256 with GQA: attn_fwd_split groups the heads of a KV
+    group into one row space; the result matches attn_fwd (which does not)
+    within the bar, and the oracle."""
+    q, k, v = _qkv(1, 16, 2, 200, 200, 128, seed=80)
+    o1, l1 = attn.attn_fwd(q, k, v, causal=causal)
+    o2, l2 = attn.attn_fwd_split(q, k, v, causal=causal, num_splits=1)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(f64(q), f64(k), f64(v), causal)
+    assert_close(f64(o2), f64(l2), o_ref, lse_ref, what="packed split")
+    assert_close(f64(o1), f64(l1), o_ref, lse_ref, what="attn_fwd")
