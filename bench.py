@@ -30,8 +30,12 @@ KERNEL_SOURCES = ["chiplet_numa_aware_amd/csrc/attn_fwd_kernel.hpp",
 METRIC = "attn fwd TFLOP/s + % bf16 MFMA peak + L2 hit %, MHA H=128 N=128K d=128"
 # MI355X published dense bf16 MFMA peak (2.5 PFLOP/s).
 PEAK_BF16_TFLOPS = 2500.0
-MODE_NAMES = ["naive_block_first", "naive_head_first",
-              "swizzled_block_first", "swizzled_head_first"]
+_BASE_NAMES = ["naive_block_first", "naive_head_first",
+               "swizzled_block_first", "swizzled_head_first"]
+# Mode ids 0..7: the pages' four modes, and each + 4 (longest first).
+MODE_NAMES = _BASE_NAMES + [n + "_longest_first" for n in _BASE_NAMES]
+SWEEP_MODES = (0, 1, 2, 3, 7)
+PROFILE_MODES = SWEEP_MODES  # one dispatch each, in this order, per profile pass
 
 WORKLOADS = {
     # name: (B, H_Q, H_KV, N, d, causal)
@@ -207,9 +211,9 @@ PROFILE_PASSES = {
 def profile_commands(workload: str, out: str):
     """The rocprofv3 runs whose output --summarize-profile reads."""
     bench = "python3 /root/repo/bench.py"
-    one = f"{bench} --workload {workload} --steps 1 --warmup 0 --modes 0,1,2,3 --no-cpu-baseline"
+    one = f"{bench} --workload {workload} --steps 1 --warmup 0 --modes {','.join(map(str, PROFILE_MODES))} --no-cpu-baseline"
     cmds = {"trace": (f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/trace -o trace -- "
-                      f"{bench} --workload {workload} --steps 2 --warmup 1 --modes 0,1,2,3 --no-cpu-baseline")}
+                      f"{bench} --workload {workload} --steps 2 --warmup 1 --modes {','.join(map(str, PROFILE_MODES))} --no-cpu-baseline")}
     for name, ctrs in PROFILE_PASSES.items():
         cmds[name] = (f"rocprofv3 --pmc {' '.join(ctrs)} --output-format csv -d {out}/{name} -o {name} -- {one}")
     for name in ("fetch", "write"):
@@ -268,7 +272,7 @@ def summarize_profile(directory: str, workload: str):
     wr, _ = one("write")
     mf, mdur = one("mfma")
     n_modes = len(l2)
-    if not (len(fe) == len(wr) == len(mf) == n_modes == 4):
+    if not (len(fe) == len(wr) == len(mf) == n_modes == len(PROFILE_MODES)):
         raise SystemExit("expected one dispatch per mapping mode in every pass")
     # Kernel-trace statistics (average duration of the attention kernel).
     trace = glob.glob(os.path.join(directory, "trace", "*_kernel_stats.csv"))
@@ -286,7 +290,7 @@ def summarize_profile(directory: str, workload: str):
         # GRBM_GUI_ACTIVE sums the busy cycles of every XCD.
         clock = gui / 8.0 / mdur[m] / 1e9
         simd_cycles = gui / 8.0 * 1024  # 256 CUs x 4 SIMDs
-        modes[MODE_NAMES[m]] = {
+        modes[MODE_NAMES[PROFILE_MODES[m]]] = {
             "l2_hit_pct": round(100.0 * hit / (hit + miss), 2),
             "fetch_bytes": fetch_b, "write_bytes": write_b,
             "hbm_bytes": fetch_b + write_b,
@@ -318,7 +322,7 @@ def summarize_profile(directory: str, workload: str):
         if "attn_fwd_kernel" in r["Name"]:
             lines.append(f"| {r['Name'].split('(')[0]} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.2f} | "
                          f"{float(r['MinNs']) / 1e6:.2f} | {float(r['MaxNs']) / 1e6:.2f} |")
-    lines += ["", "(the trace mixes the four mapping modes, 3 calls each: see the per-mode table)", "",
+    lines += ["", f"(the trace mixes the {len(PROFILE_MODES)} mapping modes, 3 calls each: see the per-mode table)", "",
               "## Counters per mapping mode (one dispatch each)", "",
               "| mode | L2 hit % | HBM read GB | HBM write GB | read / unique | MFMA busy % | clock GHz | kernel ms | TFLOP/s |",
               "|---|---|---|---|---|---|---|---|---|"]
@@ -360,7 +364,7 @@ def run_sweep(out_path: str):
         lse = torch.empty(B, H_Q, N, device="cuda", dtype=torch.float32)
         steps = 10 if N <= 32768 else 5
         res = {}
-        for mode in range(4):
+        for mode in SWEEP_MODES:
             r = time_mode(attn, q, k, v, o, lse, causal, mode, steps, 2, flops)
             res[MODE_NAMES[mode]] = flops / (r["kernel_ms_median"] / 1e3) / 1e12
             log(f"  {name:24s} {MODE_NAMES[mode]:22s} {r['kernel_ms_median']:9.3f} ms "
@@ -373,12 +377,14 @@ def run_sweep(out_path: str):
              "calls (10 when N <= 32K) after 2 warmup calls, seed 1000; "
              f"TFLOP/s = algorithmic FLOP / median; % of the {PEAK_BF16_TFLOPS:.0f} TFLOP/s "
              "bf16 peak in parentheses for swizzled head-first.", "",
-             "| configuration | TFLOP | NBF | NHF | SBF | SHF | SHF / NBF |",
-             "|---|---|---|---|---|---|---|"]
+             "SHF+LF is swizzled head-first with the longest-first row-block order (mode 7).", "",
+             "| configuration | TFLOP | NBF | NHF | SBF | SHF | SHF / NBF | SHF+LF |",
+             "|---|---|---|---|---|---|---|---|"]
     for name, flops, res in rows:
-        t = [res[m] for m in MODE_NAMES]
+        t = [res[MODE_NAMES[m]] for m in SWEEP_MODES]
         lines.append(f"| {describe(name)} | {flops / 1e12:.2f} | {t[0]:.0f} | {t[1]:.0f} | {t[2]:.0f} | "
-                     f"{t[3]:.0f} ({100 * t[3] / PEAK_BF16_TFLOPS:.1f}%) | {t[3] / t[0]:.2f} |")
+                     f"{t[3]:.0f} ({100 * t[3] / PEAK_BF16_TFLOPS:.1f}%) | {t[3] / t[0]:.2f} | "
+                     f"{t[4]:.0f} ({100 * t[4] / PEAK_BF16_TFLOPS:.1f}%) |")
     split_rows = []
     for name, (B, H_Q, H_KV, N_q, N_kv, d, causal, S) in SPLIT_WORKLOADS.items():
         q = inputs.normal_bf16((B, H_Q, N_q, d), 1000, "cuda")

@@ -325,7 +325,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // a unit is at causal position r mod pos_mod (pos_mod = N_q).
   // The remap sees M_q * num_splits row blocks per unit: m' = split * M_q +
   // row block, so the workgroups of one key range are adjacent.
-  const WgCoord wc = wg_map(mapping, blockIdx.x, B, H_U, M_q * num_splits, num_xcd);
+  const WgCoord wc = wg_map(mapping, blockIdx.x, B, H_U, M_q * num_splits, num_xcd,
+                            (uint32_t)(H_U / H_KV));
   const int kvh = (int)wc.h / (H_U / H_KV);
   const int split = (int)wc.m / M_q;
   const int row0 = ((int)wc.m - split * M_q) * kBlockM;

@@ -153,7 +153,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   if (rc != ATTN_OK) return rc;
   rc = check_head_dim(N_kv, d);
   if (rc != ATTN_OK) return rc;
-  if (mapping < 0 || mapping > 3) return ATTN_E_MAPPING;
+  if (mapping < 0 || mapping > 7) return ATTN_E_MAPPING;
   if (num_splits > 1 && (!o_ws || !lse_ws)) return ATTN_E_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (lse && !aligned16(lse)) || (num_splits > 1 && (!aligned16(o_ws) || !aligned16(lse_ws))))
@@ -188,11 +188,11 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
 // Placement probe: one wave per workgroup; lane 0 records the XCC id the
 // workgroup runs on and the coordinates the remap gives it.
 __global__ void probe_kernel(int32_t* out, int B, int H_Q, int M, int mapping,
-                             int X) {
+                             int X, int G) {
   if (threadIdx.x != 0) return;
   uint32_t xcc;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-  const WgCoord c = wg_map(mapping, blockIdx.x, B, H_Q, M, X);
+  const WgCoord c = wg_map(mapping, blockIdx.x, B, H_Q, M, X, G);
   int32_t* p = out + 4 * (uint64_t)blockIdx.x;
   p[0] = (int32_t)(xcc & 0xF);
   p[1] = (int32_t)c.b;
@@ -254,10 +254,10 @@ int attn_wg_map(int mapping, int B, int H_Q, int H_KV, int N, int num_xcd,
   int rc = check_shape(B, H_Q, H_KV, N, &M, &W);
   if (rc != ATTN_OK) return rc;
   if (num_xcd < 1) return ATTN_E_SHAPE;
-  if (mapping < 0 || mapping > 3) return ATTN_E_MAPPING;
+  if (mapping < 0 || mapping > 7) return ATTN_E_MAPPING;
   for (int w = 0; w < W; ++w) {
     const WgCoord c = wg_map(mapping, (uint32_t)w, (uint32_t)B, (uint32_t)H_Q,
-                             (uint32_t)M, (uint32_t)num_xcd);
+                             (uint32_t)M, (uint32_t)num_xcd, (uint32_t)(H_Q / H_KV));
     out_host[3 * (int64_t)w + 0] = (int32_t)c.b;
     out_host[3 * (int64_t)w + 1] = (int32_t)c.h;
     out_host[3 * (int64_t)w + 2] = (int32_t)c.m;
@@ -279,14 +279,14 @@ int attn_probe_placement(int mapping, int B, int H_Q, int H_KV, int N,
   int M = 0, W = 0;
   int rc = check_shape(B, H_Q, H_KV, N, &M, &W);
   if (rc != ATTN_OK) return rc;
-  if (mapping < 0 || mapping > 3) return ATTN_E_MAPPING;
+  if (mapping < 0 || mapping > 7) return ATTN_E_MAPPING;
   if (!aligned16(dev_out)) return ATTN_E_ALIGN;
   int X = 1;
   rc = resolve_xcd(&X);
   if (rc != ATTN_OK) return rc;
   hipLaunchKernelGGL(probe_kernel, dim3(W), dim3(64), 0,
                      static_cast<hipStream_t>(stream), dev_out, B, H_Q, M,
-                     mapping, X);
+                     mapping, X, H_Q / H_KV);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "attn_probe_placement launch");
   return ATTN_OK;
@@ -300,7 +300,7 @@ const char* attn_strerror(int code) {
       return "bad shape (B, H_Q, H_KV, N must be > 0, H_Q % H_KV == 0, "
              "B*H_Q*ceil(N/256) < 2^31, N*d*2 <= 2^31 - 2^16, num_xcd >= 1)";
     case ATTN_E_HEAD_DIM: return "unsupported head dim (need 8 <= d <= 128, d % 8 == 0)";
-    case ATTN_E_MAPPING: return "mapping must be 0..3";
+    case ATTN_E_MAPPING: return "mapping must be 0..7";
     case ATTN_E_ALIGN: return "device pointer not 16-byte aligned";
     case ATTN_E_HIP:
       return g_err_text[0] ? g_err_text : "HIP runtime error";

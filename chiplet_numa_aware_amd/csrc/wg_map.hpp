@@ -12,11 +12,20 @@
 //   * §3 before/after table and §7 Figures 3 and 11: the block-first and
 //     head-first orders and the chiplet swizzle.
 //
-// The four modes are two independent bits:
+// The four modes of the pages are two independent bits:
 //   bit 0  order    0 = block-first (heads fastest), 1 = head-first (row
 //                   blocks fastest, so an ACC is a contiguous id range)
 //   bit 1  swizzle  0 = logical id = w, 1 = XCD x = w mod X takes the x-th
 //                   contiguous slice of the logical order, in order.
+// A third bit, not on the pages, orders the work for causal attention:
+//   bit 2  longest first: row blocks are taken from the last (the most keys
+//                   under a causal mask) to the first, and in the head-first
+//                   order the G query heads of an ACC that share a row block
+//                   are adjacent (ACC, then row block, then head).
+// Under a causal mask, row blocks differ in length; taken shortest first,
+// the workgroups that share an XCD start at staggered times and drift apart
+// in the K/V stream beyond what L2 holds.  Taken longest first, a workgroup
+// that starts later is shorter, so concurrent workgroups stay close together.
 // Batch is the outermost index in both orders.  Slices are balanced (their
 // lengths differ by at most one), which is also the fallback when X does not
 // divide the number of ACCs: every XCD still walks its ACCs in one run and an
@@ -38,6 +47,7 @@ enum Mapping : int {
   kNaiveHeadFirst = 1,
   kSwizzledBlockFirst = 2,
   kSwizzledHeadFirst = 3,
+  kLongestFirst = 4,  // bit, combined with any of the above
 };
 
 constexpr int kBlockM = 256;  // query rows per workgroup (row-block height)
@@ -55,22 +65,30 @@ ATTN_HD uint32_t chiplet_slice_index(uint32_t w, uint32_t W, uint32_t X) {
   return x * base + (x < extra ? x : extra) + w / X;
 }
 
-// All arguments are assumed validated: W = B*H_Q*M < 2^31, X >= 1, w < W.
+// All arguments are assumed validated: W = B*H_Q*M < 2^31, X >= 1, w < W,
+// G (query heads per ACC) >= 1 divides H_Q.
 ATTN_HD WgCoord wg_map(int mapping, uint32_t w, uint32_t B, uint32_t H_Q,
-                       uint32_t M, uint32_t X) {
+                       uint32_t M, uint32_t X, uint32_t G) {
   const uint32_t per_batch = H_Q * M;
   const uint32_t L =
       (mapping & 2) ? chiplet_slice_index(w, B * per_batch, X) : w;
   WgCoord c;
   c.b = L / per_batch;
   const uint32_t r = L - c.b * per_batch;
-  if (mapping & 1) {  // head-first
+  uint32_t m;
+  if ((mapping & 1) && (mapping & kLongestFirst)) {  // ACC, block, head
+    const uint32_t acc = r / (G * M);
+    const uint32_t s = r - acc * (G * M);
+    m = s / G;
+    c.h = acc * G + (s - m * G);
+  } else if (mapping & 1) {  // head-first
     c.h = r / M;
-    c.m = r - c.h * M;
+    m = r - c.h * M;
   } else {  // block-first
-    c.m = r / H_Q;
-    c.h = r - c.m * H_Q;
+    m = r / H_Q;
+    c.h = r - m * H_Q;
   }
+  c.m = (mapping & kLongestFirst) ? M - 1 - m : m;
   return c;
 }
 

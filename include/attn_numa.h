@@ -37,7 +37,7 @@ extern "C" {
 #define ATTN_E_SHAPE (-2)       /* B, H_Q, H_KV or N <= 0, H_Q % H_KV != 0,
                                    or a size beyond the 32-bit limits below */
 #define ATTN_E_HEAD_DIM (-3)    /* d <= 0, d > 128 or d % 8 != 0 */
-#define ATTN_E_MAPPING (-4)     /* mapping not in 0..3 */
+#define ATTN_E_MAPPING (-4)     /* mapping not in 0..7 */
 #define ATTN_E_ALIGN (-5)       /* a device pointer is not 16-byte aligned */
 #define ATTN_E_HIP (-6)         /* HIP runtime or launch error */
 #define ATTN_E_NO_DEVICE (-7)   /* no HIP device is visible */
@@ -48,6 +48,12 @@ extern "C" {
 #define ATTN_MAP_SWIZZLED_BLOCK_FIRST 2 /* chiplet swizzle, heads fastest */
 #define ATTN_MAP_SWIZZLED_HEAD_FIRST 3  /* chiplet swizzle, blocks fastest:
                                            one ACC per XCD at a time */
+/* Added to any mode: row blocks from the last to the first (longest first
+   under a causal mask) and, in head-first order, the query heads of an ACC
+   that share a row block adjacent.  Not on the pages: concurrent workgroups
+   of a causal ACC then stay close together in the K/V stream, which keeps
+   the swizzled head-first L2 hit rate up (measured in the design notes). */
+#define ATTN_MAP_LONGEST_FIRST 4
 
 /*
  * attn_fwd: attention forward pass.
@@ -67,7 +73,8 @@ extern "C" {
  *        64-wide tile, else a 128-wide one); B*H_Q*ceil(N/256) < 2^31 and
  *        N*d*2 <= 2^31 - 2^16 bytes per head
  *   causal  0: every key; 1: query row i sees keys 0..i (top-left aligned)
- *   mapping ATTN_MAP_* (0..3); the XCD count used is attn_num_xcd()
+ *   mapping ATTN_MAP_* (0..3), optionally | ATTN_MAP_LONGEST_FIRST; the XCD
+ *          count used is attn_num_xcd()
  *   stream  hipStream_t or NULL
  *
  * Arithmetic: bf16 inputs, fp32 scores, softmax statistics and accumulators;

@@ -38,6 +38,14 @@ Readings (the pages are silent or their printed form is not a bijection):
   an ACC is split between neighbouring XCDs only where a slice boundary falls
   inside it.
 
+Added (not on the pages): LONGEST_FIRST, a causal-aware order.  Row blocks
+are taken last to first (the most visible keys first under a causal mask)
+and, head-first, the G query heads of an ACC sharing a row block are
+adjacent.  Pinned by properties (bijection; the ACC-per-XCD structure of the
+base mode is kept; within each ACC the row blocks run in non-increasing
+order with a row block's heads adjacent; with G = 1 it is the base mode with
+m reversed).
+
 Parity status: pinned.  On the domain where the pages print formulas (one
 batch, X dividing H_Q, X dividing W) tests/test_wg_map_oracle.py checks
 equality with those formulas restated from the pages, and the invariants the
@@ -81,23 +89,40 @@ def _decode(L: int, H_Q: int, M: int, head_first: bool):
     return b, h, m
 
 
+# Added to a mode: causal-aware order (not on the pages).  Row blocks are
+# taken last to first, i.e. longest first under a causal mask, and in the
+# head-first order an ACC's G query heads that share a row block are adjacent
+# (ACC, then row block, then head within the KV group).
+LONGEST_FIRST = 4
+
+
 def wg_map(mode: int, w: int, B: int, H_Q: int, N: int, X: int,
-           block_m: int = 128):
-    """(b, h_q, m) computed by linear workgroup id ``w`` under ``mode``."""
+           block_m: int = 128, G: int = 1):
+    """(b, h_q, m) computed by linear workgroup id ``w`` under ``mode``
+    (0..3, optionally + LONGEST_FIRST); G = query heads per KV group."""
     M = row_blocks(N, block_m)
     W = B * H_Q * M
     if not 0 <= w < W:
         raise ValueError("workgroup id out of range")
-    if mode in (SBF, SHF):
-        L = chiplet_swizzle(w, W, X)
-    elif mode in (NBF, NHF):
-        L = w
+    if not 0 <= mode <= 7 or H_Q % G:
+        raise ValueError("unknown mapping mode or G")
+    base, longest_first = mode & 3, bool(mode & LONGEST_FIRST)
+    L = chiplet_swizzle(w, W, X) if base in (SBF, SHF) else w
+    head_first = base in (NHF, SHF)
+    if longest_first and head_first:
+        b, r = divmod(L, H_Q * M)
+        acc, s = divmod(r, G * M)
+        m, hg = divmod(s, G)
+        h = acc * G + hg
     else:
-        raise ValueError("unknown mapping mode")
-    return _decode(L, H_Q, M, head_first=mode in (NHF, SHF))
+        b, h, m = _decode(L, H_Q, M, head_first)
+    if longest_first:
+        m = M - 1 - m
+    return b, h, m
 
 
-def wg_table(mode: int, B: int, H_Q: int, N: int, X: int, block_m: int = 128):
+def wg_table(mode: int, B: int, H_Q: int, N: int, X: int, block_m: int = 128,
+             G: int = 1):
     """List of (b, h, m) for w = 0..W-1."""
     W = num_workgroups(B, H_Q, N, block_m)
-    return [wg_map(mode, w, B, H_Q, N, X, block_m) for w in range(W)]
+    return [wg_map(mode, w, B, H_Q, N, X, block_m, G) for w in range(W)]

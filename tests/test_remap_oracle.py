@@ -213,3 +213,70 @@ def test_printed_batch_term_needs_the_batch_outer_reading():
         batch = (w // (M * H_Q)) % B
         seen.add((batch, head, block))
     assert len(seen) < B * H_Q * M
+
+
+# ---- LONGEST_FIRST (causal-aware order; not on the pages) -------------------
+def _lf_shapes():
+    shapes = [(1, 8, 8, 1024 * 8, 8), (1, 64, 8, 16384, 8), (2, 32, 4, 8192, 8),
+              (1, 12, 12, 8192, 8), (1, 8, 1, 4096, 8), (3, 6, 2, 1000, 4)]
+    return shapes + list(_random_shapes(60, seed=7))
+
+
+@pytest.mark.parametrize("base", [NBF, NHF, SBF, SHF])
+def test_longest_first_is_a_bijection(base):
+    for B, H_Q, H_KV, N, X in _lf_shapes():
+        G = H_Q // H_KV
+        tab = oracle.wg_table(base | oracle.LONGEST_FIRST, B, H_Q, N, X, G=G)
+        assert len(set(tab)) == len(tab) == oracle.num_workgroups(B, H_Q, N)
+
+
+@pytest.mark.parametrize("base", [NBF, NHF, SBF, SHF])
+def test_longest_first_with_one_head_per_acc_reverses_row_blocks(base):
+    for B, H_Q, H_KV, N, X in _lf_shapes():
+        M = oracle.row_blocks(N)
+        a = oracle.wg_table(base, B, H_Q, N, X, G=1)
+        b = oracle.wg_table(base | oracle.LONGEST_FIRST, B, H_Q, N, X, G=1)
+        assert b == [(bb, h, M - 1 - m) for bb, h, m in a]
+
+
+def test_longest_first_keeps_acc_per_xcd_and_orders_each_acc():
+    """SHF + LONGEST_FIRST: the XCD that owns each workgroup is the one SHF
+    gives it (same ACC slices); within an ACC the workgroups an XCD runs go
+    from the last row block to the first, each row block's G heads adjacent."""
+    for B, H_Q, H_KV, N, X in _lf_shapes():
+        G = H_Q // H_KV
+        M = oracle.row_blocks(N)
+        W = oracle.num_workgroups(B, H_Q, N)
+        lf = SHF | oracle.LONGEST_FIRST
+        acc_of = lambda b, h: b * H_KV + h // G
+        owner_shf = defaultdict(set)
+        for w in range(W):
+            b, h, m = oracle.wg_map(SHF, w, B, H_Q, N, X)
+            owner_shf[acc_of(b, h)].add(w % X)
+        seq = defaultdict(list)                   # per XCD, in dispatch order
+        for w in range(W):
+            b, h, m = oracle.wg_map(lf, w, B, H_Q, N, X, G=G)
+            seq[w % X].append((acc_of(b, h), m, h))
+        owner_lf = defaultdict(set)
+        for x, items in seq.items():
+            for a, m, h in items:
+                owner_lf[a].add(x)
+            by_acc = defaultdict(list)
+            for a, m, h in items:
+                by_acc[a].append((m, h))
+            for a, ms in by_acc.items():
+                assert all(ms[i][0] >= ms[i + 1][0] for i in range(len(ms) - 1)), (a, x)
+                # a row block's heads are adjacent within the ACC's run
+                seen = set()
+                for i, (m, h) in enumerate(ms):
+                    if i and ms[i - 1][0] != m:
+                        assert m not in seen
+                        seen.add(ms[i - 1][0])
+        if (B * H_KV) % X == 0:
+            assert all(len(s) == 1 for s in owner_lf.values())
+        assert {a: len(s) for a, s in owner_lf.items()} == {a: len(s) for a, s in owner_shf.items()}
+
+
+def test_longest_first_rejects_bad_mode():
+    with pytest.raises(ValueError):
+        oracle.wg_map(8, 0, 1, 8, 1024, 8)
