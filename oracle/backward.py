@@ -1,0 +1,65 @@
+"""fp64 CPU oracle for the attention backward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no code
+with the HIP kernels.
+
+What it computes: the gradients of the attention forward pass of "Optimizing
+Attention on GPUs by Exploiting GPU Architectural NUMA Effects", §4 equation
+(S = Q Kᵀ / √d, P = softmax(S) row-wise, O = P V), given the upstream
+gradient dO (the pages run FlashAttention-2's backward with the same
+workgroup remaps, digest page "Backward pass" and §5; they do not restate
+its equations, so this is the gradient of the forward definition, written
+out by the chain rule):
+
+    dV = Pᵀ dO
+    dP = dO Vᵀ
+    dS = P ⊙ (dP - rowsum(dP ⊙ P))      (softmax Jacobian, row by row)
+    dQ = dS K / √d,   dK = dSᵀ Q / √d
+
+per head; with GQA a KV head's dK and dV are the sums over its query heads.
+Causal masking as in sdpa.py (masked scores have P = 0).  No tiling, no
+recomputation trick: P is formed from S directly.
+
+Parity status: pinned (central finite differences of oracle.attention on
+tiny shapes, torch float64 autograd of the math-backend SDPA, the closed
+form dQ = dK = 0 when every V row is equal, dO = 0, GQA = summed MHA; see
+tests/test_backward_oracle.py).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .sdpa import kv_head
+
+
+def _as_f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def attention_backward(q, k, v, dout, causal: bool):
+    """Gradients (dQ [B,H_Q,N,d], dK [B,H_KV,N,d], dV [B,H_KV,N,d]) of
+    sum(dout * O) with O = attention(q, k, v), float64."""
+    q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    B, H_Q, N, d = q.shape
+    H_KV = k.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    scale = 1.0 / np.sqrt(d)
+    mask = np.tril(np.ones((N, N), dtype=bool)) if causal else None
+    for b in range(B):
+        for h in range(H_Q):
+            g = kv_head(h, H_Q, H_KV)
+            s = (q[b, h] @ k[b, g].T) * scale
+            if causal:
+                s = np.where(mask, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            e = np.exp(s)
+            p = e / e.sum(axis=1, keepdims=True)
+            dv[b, g] += p.T @ dout[b, h]
+            dp = dout[b, h] @ v[b, g].T
+            ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+            dq[b, h] = (ds @ k[b, g]) * scale
+            dk[b, g] += (ds.T @ q[b, h]) * scale
+    return dq, dk, dv
