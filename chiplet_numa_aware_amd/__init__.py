@@ -1,6 +1,7 @@
-"""Python binding of libattn_numa (NUMA-aware attention forward for MI355X).
+"""Python binding of libattn_numa (NUMA-aware attention for MI355X).
 
-Argument marshalling only: every step of the attention forward pass runs in
+Argument marshalling only: every step of the attention forward and backward
+passes runs in
 the library's HIP kernels.  torch provides device memory and streams.  The
 entry points have the names of the C ABI in include/attn_numa.h:
 
@@ -8,6 +9,7 @@ entry points have the names of the C ABI in include/attn_numa.h:
 * ``attn_fwd_split(q, k, v, causal=False, num_splits=1, mapping=3, ...)``
 * ``attn_split_chunk(N_kv, num_splits)``
 * ``attn_merge(o_parts, lse_parts, o=None, lse=None)``
+* ``attn_bwd(q, k, v, o, dout, lse, causal=False, mapping=3, ...)``
 * ``attn_wg_map(mapping, B, H_Q, H_KV, N, num_xcd)``
 * ``attn_num_xcd()``
 * ``attn_block_m()``
@@ -26,7 +28,7 @@ import numpy as np
 import torch  # first, so the library binds to the HIP runtime torch loaded
 
 __all__ = [
-    "AttnError", "attn_fwd", "attn_fwd_split", "attn_split_chunk", "attn_merge",
+    "AttnError", "attn_fwd", "attn_fwd_split", "attn_split_chunk", "attn_merge", "attn_bwd",
     "attn_wg_map", "attn_num_xcd", "attn_block_m",
     "attn_probe_placement", "attn_strerror", "library_path", "load_library",
     "MAPPINGS", "row_blocks", "num_workgroups", "BLOCK_M",
@@ -74,6 +76,8 @@ def load_library():
     lib.attn_split_chunk.restype = i32
     lib.attn_merge.argtypes = [vp, vp] + [i32] * 5 + [vp, vp, vp]
     lib.attn_merge.restype = i32
+    lib.attn_bwd.argtypes = [vp] * 10 + [i32] * 7 + [vp]
+    lib.attn_bwd.restype = i32
     lib.attn_wg_map.argtypes = [i32] * 6 + [vp]
     lib.attn_wg_map.restype = i32
     lib.attn_num_xcd.argtypes = []
@@ -259,6 +263,46 @@ def attn_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,
                             _stream_handle(stream, o_parts.device))
     _check(rc, "attn_merge")
     return o, lse
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+             dout: torch.Tensor, lse: torch.Tensor, causal: bool = False, mapping=3,
+             dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+             dv: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+             stream: torch.cuda.Stream | None = None):
+    """Gradients (dq, dk, dv) of sum(dout * o) for o, lse = attn_fwd(q, k, v,
+    causal).  q, o, dout [B,H_Q,N,d] and k, v [B,H_KV,N,d] contiguous bf16;
+    lse fp32 [B,H_Q,N].  Outputs and the fp32 workspace ws [2,B,H_Q,N] are
+    allocated when not given.  Enqueued on ``stream``; returns without
+    synchronising."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_bf16(name, t)
+    B, H_Q, N, d = q.shape
+    H_KV = k.shape[1]
+    if k.shape != (B, H_KV, N, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H_KV, N, d] with q's B, N, d")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must be shaped like q")
+    _check_f32("lse", lse, (B, H_Q, N))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_bf16(name, t)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} must have shape {tuple(ref.shape)}")
+    if ws is None:
+        ws = torch.empty((2, B, H_Q, N), dtype=torch.float32, device=q.device)
+    _check_f32("ws", ws, (2, B, H_Q, N))
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                          dv.data_ptr(), ws.data_ptr(), B, H_Q, H_KV, N, d,
+                          int(bool(causal)), _mapping_id(mapping),
+                          _stream_handle(stream, q.device))
+    _check(rc, "attn_bwd")
+    return dq, dk, dv
 
 
 def attn_wg_map(mapping, B: int, H_Q: int, H_KV: int, N: int,

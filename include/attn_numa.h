@@ -151,6 +151,45 @@ int attn_merge(const float* o_parts, const float* lse_parts, int num_splits,
                void* stream);
 
 /*
+ * attn_bwd: gradients dQ, dK, dV of sum(dO * O) for the attention of
+ * attn_fwd (FlashAttention-2 style: P is recomputed from q, k and the
+ * forward's lse), with the same workgroup remap as the forward pass.
+ *
+ * Passage: digest page, Q3 results table and the §3 "Backward pass"
+ * paragraph (the paper's Figure 16: the remaps applied to FA2's backward
+ * kernel); the equations are the chain rule of the §4 equation:
+ * dV = P^T dO, dP = dO V^T, dS = P * (dP - D) with D = rowsum(dO * O),
+ * dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d); with GQA a KV head's dK, dV
+ * sum over its query heads.
+ *
+ *   q, o, dout  device, bf16 [B][H_Q][N][d], read only (o: attn_fwd's output)
+ *   k, v        device, bf16 [B][H_KV][N][d], read only
+ *   lse         device, fp32 [B][H_Q][N], read only: attn_fwd's lse (natural log)
+ *   dq          device, bf16 [B][H_Q][N][d], written (every element)
+ *   dk, dv      device, bf16 [B][H_KV][N][d], written (every element)
+ *   ws          device, fp32 [2][B][H_Q][N], caller-owned workspace:
+ *               lse * log2(e), then D; overwritten
+ *   B, H_Q, H_KV, N, d, causal   as attn_fwd (the same mask); also
+ *               B*H_Q*ceil(N/128) < 2^31
+ *   mapping     ATTN_MAP_* (0..7) as attn_fwd: the dK/dV kernel maps
+ *               (batch, KV head, 128-key block) with the remap's row blocks
+ *               counted from the last key block (the fewest query rows under
+ *               a causal mask), the dQ kernel (batch, query head, 128-row block)
+ *   stream      hipStream_t or NULL
+ * Launches three kernels on `stream` (D and lse2 per row; dK and dV; dQ).
+ * Arithmetic: bf16 inputs, fp32 scores and accumulators; P and dS are rounded
+ * to bf16 (nearest-even) before the products that use them; outputs are
+ * rounded to bf16.  Deterministic: every output element is reduced by one
+ * workgroup in a fixed order, so results do not depend on `mapping`.
+ * Errors: ATTN_E_NULL (any pointer NULL), ATTN_E_SHAPE, ATTN_E_HEAD_DIM,
+ * ATTN_E_MAPPING, ATTN_E_ALIGN (any pointer), ATTN_E_NO_DEVICE, ATTN_E_HIP.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+             float* ws, int B, int H_Q, int H_KV, int N, int d, int causal,
+             int mapping, void* stream);
+
+/*
  * attn_wg_map: the remap table the kernel uses, computed on the host.
  *
  * Passage: digest page §2 Q1 (dispatch to XCD w mod X), §2 Q2 and §7

@@ -35,7 +35,7 @@ def _declared_codes():
 def test_library_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_split", "attn_split_chunk", "attn_merge",
-                          "attn_wg_map", "attn_num_xcd", "attn_block_m",
+                          "attn_bwd", "attn_wg_map", "attn_num_xcd", "attn_block_m",
                           "attn_probe_placement", "attn_strerror"}
     for n in names:
         assert hasattr(lib, n), n
@@ -200,3 +200,28 @@ def test_split_and_merge_argument_errors(lib):
     assert m(N=0) == c["ATTN_E_SHAPE"]
     assert m(d=7) == c["ATTN_E_HEAD_DIM"]
     assert m(lp=FAKE + 8) == c["ATTN_E_ALIGN"]
+
+
+def test_bwd_argument_errors(lib):
+    """attn_bwd rejects bad arguments before anything could launch on the
+    fake pointers (every case below fails a host check)."""
+    c = _declared_codes()
+
+    def b(**kw):
+        ptrs = [kw.get(n, FAKE) for n in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws")]
+        return lib.attn_bwd(*ptrs, kw.get("B", 1), kw.get("H_Q", 4), kw.get("H_KV", 2),
+                            kw.get("N", 300), kw.get("d", 128), kw.get("causal", 1),
+                            kw.get("mapping", 8 if "mapping_ok" not in kw else 3), None)
+
+    for n in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws"):
+        assert b(**{n: None}) == c["ATTN_E_NULL"], n
+    for kw in ({"N": 0}, {"B": 0}, {"H_Q": 6, "H_KV": 4}, {"H_KV": 0},
+               {"B": 1 << 12, "H_Q": 1 << 12, "H_KV": 1 << 12, "N": 1 << 14},
+               {"N": (1 << 31) // 256 + 1}):
+        assert b(**kw) == c["ATTN_E_SHAPE"], kw
+    for d in (0, 12, 136):
+        assert b(d=d) == c["ATTN_E_HEAD_DIM"], d
+    assert b() == c["ATTN_E_MAPPING"]          # mapping 8
+    assert b(mapping=-1) == c["ATTN_E_MAPPING"]
+    for n in ("q", "dout", "lse", "dk", "ws"):
+        assert b(mapping_ok=1, **{n: FAKE + 4}) == c["ATTN_E_ALIGN"], n

@@ -1,0 +1,106 @@
+"""Attention backward (attn_bwd) on the GPU against the fp64 oracle
+(oracle/backward.py), through the C ABI.
+
+The GPU gradients use the GPU forward's bf16 O and fp32 lse, as a training
+step would; the oracle differentiates the exact attention.  Bar per tensor
+(dQ, dK, dV), from the rounding steps of the kernels (bf16 P and dS before
+their products, D from the bf16 O, bf16 outputs; see the design notes):
+relative L2 error <= BWD_REL_L2 and max|err| <= BWD_MAX_REL * max|ref|.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import chiplet_numa_aware_amd as attn
+import oracle
+from chiplet_numa_aware_amd import inputs
+from tests.gpu_util import f64, say
+
+pytestmark = pytest.mark.gpu
+
+BWD_REL_L2 = 1e-2
+BWD_MAX_REL = 2e-2
+
+
+def grad_inputs(B, H_Q, H_KV, N, d, seed):
+    q, k, v = inputs.make_qkv(B, H_Q, H_KV, N, d, seed, "cuda")
+    dout = inputs.normal_bf16((B, H_Q, N, d), seed + 3, "cuda")
+    return q, k, v, dout
+
+
+def check_grad(got, ref, what):
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    denom = float(np.linalg.norm(ref))
+    err = got - ref
+    rel = float(np.linalg.norm(err)) / denom if denom > 0 else float(np.abs(err).max())
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    mx = float(np.abs(err).max()) if err.size else 0.0
+    say(f"  {what}: relL2={rel:.3e} max|err|={mx:.3e} (max|ref| {scale:.3e})")
+    assert rel <= BWD_REL_L2, f"{what}: rel-L2 {rel}"
+    assert mx <= BWD_MAX_REL * max(scale, 1e-30), f"{what}: max|err| {mx} vs max|ref| {scale}"
+
+
+CASES = [
+    # B, H_Q, H_KV, N, d, causal
+    (1, 2, 2, 300, 128, False),
+    (1, 2, 2, 300, 128, True),
+    (2, 4, 2, 257, 64, True),      # GQA, ragged tail, d = 64
+    (1, 4, 1, 200, 56, False),     # d = 56 runs the 64-wide tile
+    (1, 2, 1, 333, 96, True),      # d = 96 runs the 128-wide tile
+    (1, 2, 2, 32, 128, True),      # one tile
+    (1, 3, 3, 1, 128, False),      # one row
+    (1, 2, 2, 129, 64, True),      # one key past a 128-key block
+    (1, 8, 2, 700, 128, True),     # GQA 4 heads per KV head, several blocks
+    (1, 1, 1, 1030, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=str)
+def test_backward_matches_oracle(case):
+    B, H_Q, H_KV, N, d, causal = case
+    say(f"case bwd {case}")
+    q, k, v, dout = grad_inputs(B, H_Q, H_KV, N, d, seed=900 + N + d)
+    o, lse = attn.attn_fwd(q, k, v, causal=causal)
+    dq, dk, dv = attn.attn_bwd(q, k, v, o, dout, lse, causal=causal)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(f64(q), f64(k), f64(v), f64(dout), causal)
+    check_grad(f64(dq), rq, f"dQ {case}")
+    check_grad(f64(dk), rk, f"dK {case}")
+    check_grad(f64(dv), rv, f"dV {case}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_bitwise_identical_across_mappings(causal):
+    q, k, v, dout = grad_inputs(2, 8, 2, 1000, 128, seed=910)
+    o, lse = attn.attn_fwd(q, k, v, causal=causal)
+    ref = None
+    for mapping in range(8):
+        dq, dk, dv = attn.attn_bwd(q, k, v, o, dout, lse, causal=causal, mapping=mapping)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = (dq.clone(), dk.clone(), dv.clone())
+        else:
+            for a, b, name in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+                assert torch.equal(a, b), (mapping, name)
+
+
+def test_backward_writes_every_element():
+    """Outputs prefilled with NaN come back finite (every element written)."""
+    B, H_Q, H_KV, N, d = 1, 4, 2, 390, 120
+    q, k, v, dout = grad_inputs(B, H_Q, H_KV, N, d, seed=920)
+    o, lse = attn.attn_fwd(q, k, v, causal=True)
+    dq = torch.full_like(q, float("nan"))
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    ws = torch.full((2, B, H_Q, N), float("nan"), device="cuda")
+    attn.attn_bwd(q, k, v, o, dout, lse, causal=True, dq=dq, dk=dk, dv=dv, ws=ws)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    rq, rk, rv = oracle.attention_backward(f64(q), f64(k), f64(v), f64(dout), True)
+    check_grad(f64(dq), rq, "dQ d=120")
+    check_grad(f64(dk), rk, "dK d=120")
+    check_grad(f64(dv), rv, "dV d=120")
