@@ -11,6 +11,8 @@ Head-first.  Prints ONE JSON line on stdout (progress goes to stderr).
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--modes 0,1,2,3] [--no-cpu-baseline]
   python bench.py --sweep OUT.md    every configuration x mapping mode, timed
+  python bench.py --pass bwd [--workload NAME]   the backward pass (attn_bwd):
+                  dQ, dK, dV from the forward's O and lse, one JSON line
 """
 from __future__ import annotations
 
@@ -23,9 +25,19 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["chiplet_numa_aware_amd/csrc/attn_fwd_kernel.hpp",
-                  "chiplet_numa_aware_amd/csrc/wg_map.hpp",
-                  "chiplet_numa_aware_amd/csrc/attn_numa.hip"]
+KERNEL_SOURCES = {
+    "fwd": ["chiplet_numa_aware_amd/csrc/attn_fwd_kernel.hpp",
+            "chiplet_numa_aware_amd/csrc/wg_map.hpp",
+            "chiplet_numa_aware_amd/csrc/attn_numa.hip"],
+    "bwd": ["chiplet_numa_aware_amd/csrc/attn_bwd_kernel.hpp",
+            "chiplet_numa_aware_amd/csrc/attn_fwd_kernel.hpp",
+            "chiplet_numa_aware_amd/csrc/wg_map.hpp",
+            "chiplet_numa_aware_amd/csrc/attn_bwd.hip"],
+}
+# Kernels whose counters a profile reports, per pass.
+PASS_KERNELS = {"fwd": ["attn_fwd_kernel"],
+                "bwd": ["attn_bwd_dkv_kernel", "attn_bwd_dq_kernel"]}
+BWD_METRIC = "attn bwd TFLOP/s (dQ, dK, dV; 2.5x the forward's FLOPs) + % bf16 MFMA peak + L2 hit %"
 
 METRIC = "attn fwd TFLOP/s + % bf16 MFMA peak + L2 hit %, MHA H=128 N=128K d=128"
 # MI355X published dense bf16 MFMA peak (2.5 PFLOP/s).
@@ -95,6 +107,15 @@ def attn_flops(B, H_Q, N, d, causal) -> float:
     return 4.0 * B * H_Q * d * pairs
 
 
+def pass_flops(which, B, H_Q, N, d, causal) -> float:
+    """Forward: attn_flops.  Backward: the five products of the gradient
+    (S = Q K^T again, dV, dP, dQ, dK), 2*d each per (query, visible key),
+    i.e. 2.5x the forward (the usual convention; the kernels recompute S and
+    dP once more for dQ, which is not counted)."""
+    f = attn_flops(B, H_Q, N, d, causal)
+    return f if which == "fwd" else 2.5 * f
+
+
 def describe(name) -> str:
     B, H_Q, H_KV, N, d, causal = WORKLOADS[name]
     kind = "MHA" if H_Q == H_KV else "GQA"
@@ -102,18 +123,18 @@ def describe(name) -> str:
             f"{'causal' if causal else 'non-causal'}")
 
 
-def kernel_hash() -> str:
+def kernel_hash(which: str = "fwd") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[which]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def stored_counters(workload: str, khash: str):
+def stored_counters(workload: str, khash: str, which: str = "fwd"):
     """Counter-derived figures (L2 hit, HBM bytes) kept under profiles/ for
     this workload, or None when absent or taken on another kernel version."""
-    path = os.path.join(PROFILES, f"counters_attn_fwd_{workload}.json")
+    path = os.path.join(PROFILES, f"counters_attn_{which}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -151,6 +172,36 @@ def time_mode(attn, q, k, v, o, lse, causal, mode, steps, warmup, flops):
         "kernel_ms_median": med_ms,
         "kernel_tflops": flops / avg_kernel_s / 1e12,
         "pct_peak": 100.0 * flops / avg_kernel_s / 1e12 / PEAK_BF16_TFLOPS,
+    }
+
+
+def time_calls(call, steps, warmup, flops):
+    """`call(stream)` timed like time_mode: HIP events around each call on the
+    stream the kernels run on, and the wall clock over all of them."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        call(stream)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        call(stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    avg_s = sum(kern_ms) / len(kern_ms) / 1e3
+    return {
+        "ms_per_step": wall / steps * 1e3,
+        "tflops": flops / (wall / steps) / 1e12,
+        "kernel_ms_avg": avg_s * 1e3,
+        "kernel_ms_min": min(kern_ms),
+        "kernel_ms_median": sorted(kern_ms)[len(kern_ms) // 2],
+        "kernel_tflops": flops / avg_s / 1e12,
+        "pct_peak": 100.0 * flops / avg_s / 1e12 / PEAK_BF16_TFLOPS,
     }
 
 
@@ -208,12 +259,14 @@ PROFILE_PASSES = {
 }
 
 
-def profile_commands(workload: str, out: str):
+def profile_commands(workload: str, out: str, which: str = "fwd"):
     """The rocprofv3 runs whose output --summarize-profile reads."""
     bench = "python3 /root/repo/bench.py"
-    one = f"{bench} --workload {workload} --steps 1 --warmup 0 --modes {','.join(map(str, PROFILE_MODES))} --no-cpu-baseline"
+    modes = ",".join(map(str, PROFILE_MODES))
+    sel = f"--workload {workload}" + (" --pass bwd" if which == "bwd" else "")
+    one = f"{bench} {sel} --steps 1 --warmup 0 --modes {modes} --no-cpu-baseline"
     cmds = {"trace": (f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/trace -o trace -- "
-                      f"{bench} --workload {workload} --steps 2 --warmup 1 --modes {','.join(map(str, PROFILE_MODES))} --no-cpu-baseline")}
+                      f"{bench} {sel} --steps 2 --warmup 1 --modes {modes} --no-cpu-baseline")}
     for name, ctrs in PROFILE_PASSES.items():
         cmds[name] = (f"rocprofv3 --pmc {' '.join(ctrs)} --output-format csv -d {out}/{name} -o {name} -- {one}")
     for name in ("fetch", "write"):
@@ -237,15 +290,15 @@ def _read_counters(path, kernel_substr):
     return [vals[k] for k in sorted(vals)], [dur[k] for k in sorted(dur)]
 
 
-def _recorded_commands(directory: str, workload: str):
+def _recorded_commands(directory: str, workload: str, which: str = "fwd"):
     """The commands the profiling run executed: `commands.txt` written there
     by --print-profile-commands, else the commands for that directory."""
     path = os.path.join(directory, "commands.txt")
     if os.path.exists(path):
         with open(path) as f:
             cmds = [line.strip() for line in f if line.strip()]
-        return dict(zip(profile_commands(workload, "X").keys(), cmds))
-    return profile_commands(workload, os.path.abspath(directory))
+        return dict(zip(profile_commands(workload, "X", which).keys(), cmds))
+    return profile_commands(workload, os.path.abspath(directory), which)
 
 
 def summarize_profile(directory: str, workload: str):
@@ -349,6 +402,176 @@ def summarize_profile(directory: str, workload: str):
     print(json.dumps({k: v for k, v in data.items() if k != "commands"}, indent=1))
 
 
+def summarize_bwd_profile(directory: str, workload: str):
+    """The backward pass's rocprofv3 CSVs (profile_commands(..., "bwd")) into
+    profiles/attn_bwd_<workload>.md and counters_attn_bwd_<workload>.json:
+    per mapping mode and per gradient kernel, L2 hit rate, HBM bytes, MFMA
+    busy share, clock and duration."""
+    import csv
+    import glob
+    B, H_Q, H_KV, N, d, causal = WORKLOADS[workload]
+    flops = pass_flops("bwd", B, H_Q, N, d, causal)
+
+    def one(pass_name, kernel):
+        files = glob.glob(os.path.join(directory, pass_name, "*_counter_collection.csv"))
+        if not files:
+            raise SystemExit(f"missing {pass_name} counters under {directory}")
+        return _read_counters(files[0], kernel)
+
+    cal = {}
+    for name, ctr in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        v, _ = one("copy_" + name, "copyBuffer")
+        cal[ctr] = (1 << 30) / (v[-1][ctr] * 1024.0)
+    _, pre_durs = one("l2", "attn_bwd_pre_kernel")
+    q_bytes, kv_bytes = B * H_Q * N * d * 2, B * H_KV * N * d * 2
+    unique = {"attn_bwd_dkv_kernel": 2 * q_bytes + 4 * kv_bytes + 8 * B * H_Q * N,
+              "attn_bwd_dq_kernel": 3 * q_bytes + 2 * kv_bytes + 8 * B * H_Q * N}
+    per_kernel = {}
+    for kern in PASS_KERNELS["bwd"]:
+        l2, durs = one("l2", kern)
+        fe, _ = one("fetch", kern)
+        wr, _ = one("write", kern)
+        mf, mdur = one("mfma", kern)
+        if not (len(l2) == len(fe) == len(wr) == len(mf) == len(PROFILE_MODES)):
+            raise SystemExit(f"expected one {kern} dispatch per mapping mode in every pass")
+        rows = {}
+        for m in range(len(PROFILE_MODES)):
+            hit, miss = l2[m]["TCC_HIT_sum"], l2[m]["TCC_MISS_sum"]
+            fetch_b = fe[m]["FETCH_SIZE"] * 1024.0 * cal["FETCH_SIZE"]
+            write_b = wr[m]["WRITE_SIZE"] * 1024.0 * cal["WRITE_SIZE"]
+            gui = mf[m]["GRBM_GUI_ACTIVE"]
+            rows[MODE_NAMES[PROFILE_MODES[m]]] = {
+                "l2_hit_pct": round(100.0 * hit / (hit + miss), 2),
+                "fetch_bytes": fetch_b, "write_bytes": write_b,
+                "fetch_over_unique": round(fetch_b / unique[kern], 2),
+                "mfma_busy_pct": round(100.0 * mf[m]["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui / 8.0 * 1024), 2),
+                "clock_ghz": round(gui / 8.0 / mdur[m] / 1e9, 3),
+                "kernel_ms_counter_run": round(durs[m] * 1e3, 3),
+            }
+        per_kernel[kern] = rows
+    modes = {}
+    for m, mode in enumerate(PROFILE_MODES):
+        name = MODE_NAMES[mode]
+        total = pre_durs[m] * 1e3 + sum(per_kernel[k][name]["kernel_ms_counter_run"] for k in per_kernel)
+        modes[name] = {"ms": round(total, 3), "tflops": round(flops / (total / 1e3) / 1e12, 1),
+                       "pre_ms": round(pre_durs[m] * 1e3, 3)}
+    trace = glob.glob(os.path.join(directory, "trace", "*_kernel_stats.csv"))
+    stats = []
+    if trace:
+        with open(trace[0]) as f:
+            stats = [r for r in csv.DictReader(f) if "attn_bwd" in r["Name"]]
+    data = {
+        "kernels": ["attn_numa::attn_bwd_pre_kernel"] + [f"attn_numa::{k}" for k in PASS_KERNELS["bwd"]],
+        "kernel_hash": kernel_hash("bwd"),
+        "workload": workload, "description": describe(workload).replace(" fwd ", " bwd "),
+        "algorithmic_flops": flops, "unique_bytes": unique,
+        "calibration": {"copy_bytes": 1 << 30, "scale": cal},
+        "modes": modes, "per_kernel": per_kernel,
+        "commands": _recorded_commands(directory, workload, "bwd"),
+    }
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"counters_attn_bwd_{workload}.json"), "w") as f:
+        json.dump(data, f, indent=1)
+    lines = [f"# attn_bwd (attn_bwd_pre, attn_bwd_dkv, attn_bwd_dq), {data['description']}", "",
+             f"Kernel source hash {data['kernel_hash']} (sha256 of the backward's sources, first 16 hex).",
+             f"Algorithmic work {flops / 1e12:.1f} TFLOP per call (2.5x the forward's).", "",
+             "## rocprofv3 --kernel-trace --stats", "",
+             "| kernel | calls | average ms | min ms | max ms |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {r['Name'].split('(')[0]} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
+                     f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} |")
+    lines += ["", f"(the trace mixes the {len(PROFILE_MODES)} mapping modes, 3 calls each: see the per-mode tables)",
+              "", "## Whole backward per mapping mode (counter runs: pre + dK/dV + dQ durations)", "",
+              "| mode | ms | TFLOP/s | % of bf16 peak |", "|---|---|---|---|"]
+    for name, mm in modes.items():
+        lines.append(f"| {name} | {mm['ms']} | {mm['tflops']} | {100 * mm['tflops'] / PEAK_BF16_TFLOPS:.1f} |")
+    for kern, rows in per_kernel.items():
+        lines += ["", f"## {kern}, counters per mapping mode (one dispatch each)", "",
+                  "| mode | L2 hit % | HBM read GB | HBM write GB | read / unique | MFMA busy % | clock GHz | ms |",
+                  "|---|---|---|---|---|---|---|---|"]
+        for name, mm in rows.items():
+            lines.append(f"| {name} | {mm['l2_hit_pct']} | {mm['fetch_bytes'] / 1e9:.1f} | "
+                         f"{mm['write_bytes'] / 1e9:.2f} | {mm['fetch_over_unique']} | {mm['mfma_busy_pct']} | "
+                         f"{mm['clock_ghz']} | {mm['kernel_ms_counter_run']} |")
+    lines += ["", f"HBM bytes: FETCH_SIZE and WRITE_SIZE scaled by a plain 1 GiB copy's counts "
+              f"(read x{cal['FETCH_SIZE']:.3f}, write x{cal['WRITE_SIZE']:.3f}). Unique bytes: dK/dV "
+              "kernel Q, dO, K, V, dK, dV and the two fp32 row statistics; dQ kernel Q, dO, K, V, dQ and "
+              "the statistics.", "", "## Commands", "",
+              "Each pass is its own process, run as `cd /tmp && export TMPDIR=/tmp && <command>` "
+              "with the repository at /root/repo; then "
+              f"`python3 bench.py --workload {workload} --pass bwd --summarize-profile DIR` wrote this file.", ""]
+    for name, cmd in data["commands"].items():
+        lines.append(f"- {name}: `{cmd}`")
+    with open(os.path.join(PROFILES, f"attn_bwd_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({k: v for k, v in data.items() if k != "commands"}, indent=1))
+
+
+def run_bwd(args, attn, inputs):
+    """--pass bwd: times attn_bwd per mapping mode; prints one JSON line."""
+    import torch
+    B, H_Q, H_KV, N, d, causal = WORKLOADS[args.workload]
+    modes = [int(m) for m in args.modes.split(",") if m.strip() != ""]
+    headline = 7 if (causal and 7 in modes) else (3 if 3 in modes else modes[-1])
+    flops = pass_flops("bwd", B, H_Q, N, d, causal)
+    log(f"workload {describe(args.workload)} backward: {flops / 1e12:.1f} TFLOP per call")
+    q, k, v = inputs.make_qkv(B, H_Q, H_KV, N, d, seed=1000, device="cuda")
+    dout = inputs.normal_bf16((B, H_Q, N, d), 1003, "cuda")
+    o, lse = attn.attn_fwd(q, k, v, causal=causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((2, B, H_Q, N), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    results = {}
+    for mode in modes:
+        def call(stream, mode=mode):
+            attn.attn_bwd(q, k, v, o, dout, lse, causal=causal, mapping=mode, dq=dq, dk=dk,
+                          dv=dv, ws=ws, stream=stream)
+        r = time_calls(call, args.steps, args.warmup, flops)
+        results[mode] = r
+        log(f"  {MODE_NAMES[mode]:34s} {r['kernel_tflops']:8.1f} TFLOP/s "
+            f"({r['pct_peak']:.1f}% of peak, {r['kernel_ms_avg']:.2f} ms)")
+    counters = stored_counters(args.workload, kernel_hash("bwd"), "bwd")
+    head = results[headline]
+    modes_out = {}
+    for mode, r in results.items():
+        entry = {k2: round(v2, 4) for k2, v2 in r.items()}
+        if counters:
+            for kern, rows in counters["per_kernel"].items():
+                if MODE_NAMES[mode] in rows:
+                    entry[kern.replace("attn_bwd_", "").replace("_kernel", "") + "_l2_hit_pct"] = \
+                        rows[MODE_NAMES[mode]]["l2_hit_pct"]
+        modes_out[MODE_NAMES[mode]] = entry
+    traffic = None
+    if counters:
+        traffic = sum(rows[MODE_NAMES[headline]]["fetch_bytes"] + rows[MODE_NAMES[headline]]["write_bytes"]
+                      for rows in counters["per_kernel"].values() if MODE_NAMES[headline] in rows)
+    out = {
+        "metric": BWD_METRIC,
+        "value": round(head["kernel_tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: bf16 N(0,1) Q/K/V/dO from fixed seeds",
+        "config": {"workload": describe(args.workload).replace(" fwd ", " bwd "),
+                   "B": B, "H_Q": H_Q, "H_KV": H_KV, "N": N, "d": d, "causal": causal,
+                   "mapping": MODE_NAMES[headline], "parallelism": "single GPU"},
+        "pct_peak": round(head["pct_peak"], 2),
+        "modes": modes_out,
+        "roofline": {"bound": "mfma", "achieved": round(head["kernel_tflops"], 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(head["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "scope": "one attn_bwd call (its three kernels, one stream)"},
+        "kernel_hash": kernel_hash("bwd"),
+    }
+    if 0 in results and headline != 0:
+        out["speedup_vs_naive_block_first"] = round(
+            results[0]["kernel_ms_avg"] / head["kernel_ms_avg"], 4)
+    print(json.dumps(out), flush=True)
+
+
 def run_sweep(out_path: str):
     """Times every SWEEP configuration under the four mapping modes (2 warmup
     calls, then the median of 5 calls, 10 when N <= 32K) and writes a table."""
@@ -448,6 +671,8 @@ def main():
     ap.add_argument("--modes", default="0,1,2,3",
                     help="mapping modes to time; the last one listed that is "
                          "3 (or the last one) is the headline")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="fwd: attn_fwd (default); bwd: attn_bwd on the forward's O, lse")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--sweep", metavar="OUT_MD",
@@ -462,10 +687,13 @@ def main():
                     help="print the rocprofv3 commands for --workload, output under OUT")
     args = ap.parse_args()
     if args.summarize_profile:
-        summarize_profile(args.summarize_profile, args.workload)
+        if args.which == "bwd":
+            summarize_bwd_profile(args.summarize_profile, args.workload)
+        else:
+            summarize_profile(args.summarize_profile, args.workload)
         return
     if args.print_profile_commands:
-        for cmd in profile_commands(args.workload, args.print_profile_commands).values():
+        for cmd in profile_commands(args.workload, args.print_profile_commands, args.which).values():
             print(cmd)
         return
 
@@ -495,6 +723,9 @@ def main():
     attn.load_library()
     if args.sweep:
         run_sweep(args.sweep)
+        return
+    if args.which == "bwd":
+        run_bwd(args, attn, inputs)
         return
     B, H_Q, H_KV, N, d, causal = WORKLOADS[args.workload]
     modes = [int(m) for m in args.modes.split(",") if m.strip() != ""]

@@ -5,14 +5,14 @@ import this package.  It shares no code with the HIP path.
 """
 from .sdpa import attention, attention_head_rows, attention_sampled, kv_head
 from .split import causal_offset, merge, partial_attention, partial_head_rows
-from .backward import attention_backward
+from .backward import attention_backward, backward_key_rows, backward_query_rows
 from .remap import (NBF, NHF, SBF, SHF, LONGEST_FIRST, MODE_NAMES, chiplet_swizzle,
                      num_workgroups, row_blocks, wg_map, wg_table, xcd_of)
 
 __all__ = [
     "attention", "attention_head_rows", "attention_sampled", "kv_head",
     "causal_offset", "merge", "partial_attention", "partial_head_rows",
-    "attention_backward",
+    "attention_backward", "backward_key_rows", "backward_query_rows",
     "NBF", "NHF", "SBF", "SHF", "LONGEST_FIRST", "MODE_NAMES", "chiplet_swizzle",
     "num_workgroups", "row_blocks", "wg_map", "wg_table", "xcd_of",
 ]

@@ -24,7 +24,9 @@ recomputation trick: P is formed from S directly.
 Parity status: pinned (central finite differences of oracle.attention on
 tiny shapes, torch float64 autograd of the math-backend SDPA, the closed
 form dQ = dK = 0 when every V row is equal, dO = 0, GQA = summed MHA; see
-tests/test_backward_oracle.py).
+tests/test_backward_oracle.py).  The sampled forms below (dQ of chosen query
+rows, dK and dV of chosen keys, for long sequences) are pinned against
+attention_backward on small shapes in the same file.
 """
 from __future__ import annotations
 
@@ -63,3 +65,59 @@ def attention_backward(q, k, v, dout, causal: bool):
             dq[b, h] = (ds @ k[b, g]) * scale
             dk[b, g] += (ds.T @ q[b, h]) * scale
     return dq, dk, dv
+
+
+def _softmax_rows(q_rows, k_head, rows, causal):
+    """P (the softmax of the scaled, masked scores) of some query rows of one
+    head, float64 [R, N]; also returns the scale 1/sqrt(d)."""
+    d = q_rows.shape[1]
+    scale = 1.0 / np.sqrt(d)
+    s = (q_rows @ k_head.T) * scale
+    if causal:
+        s = np.where(np.arange(k_head.shape[0])[None, :] <= rows[:, None], s, -np.inf)
+    s = s - s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return e / e.sum(axis=1, keepdims=True), scale
+
+
+def backward_query_rows(q_rows, k_head, v_head, dout_rows, rows, causal: bool):
+    """dQ of some query rows of one head, float64 [R, d].
+
+    q_rows, dout_rows: [R, d], the rows' queries and upstream gradients;
+    k_head, v_head: [N, d] (the head's KV head); rows: [R] their positions
+    (causal mask).  dQ_i needs row i alone: dS_i = P_i * (dP_i - <dP_i, P_i>)
+    with dP_i = dO_i V^T, and dQ_i = dS_i K / sqrt(d).
+    """
+    q_rows, k_head, v_head, dout_rows = (_as_f64(x) for x in (q_rows, k_head, v_head, dout_rows))
+    rows = np.asarray(rows, dtype=np.int64)
+    p, scale = _softmax_rows(q_rows, k_head, rows, causal)
+    dp = dout_rows @ v_head.T
+    ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+    return (ds @ k_head) * scale
+
+
+def backward_key_rows(q_heads, k_head, v_head, dout_heads, keys, causal: bool,
+                      row_chunk: int = 512):
+    """dK and dV of some keys of one KV head, float64 ([K, d], [K, d]).
+
+    q_heads, dout_heads: [G, N, d], the query heads that read this KV head
+    (their contributions are summed); k_head, v_head: [N, d]; keys: [K] key
+    indices.  dV_j = sum over heads and rows i of P[i, j] dO_i, and
+    dK_j = sum of dS[i, j] Q_i / sqrt(d): every row's P and dS need that row's
+    whole score row (its normalisation), so all rows are formed; they are
+    taken ``row_chunk`` at a time only to bound memory.
+    """
+    q_heads, k_head, v_head, dout_heads = (_as_f64(x) for x in (q_heads, k_head, v_head, dout_heads))
+    keys = np.asarray(keys, dtype=np.int64)
+    G, N, d = q_heads.shape
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), d))
+    for h in range(G):
+        for r0 in range(0, N, row_chunk):
+            rows = np.arange(r0, min(N, r0 + row_chunk))
+            p, scale = _softmax_rows(q_heads[h, rows], k_head, rows, causal)
+            dp = dout_heads[h, rows] @ v_head.T
+            ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+            dv += p[:, keys].T @ dout_heads[h, rows]
+            dk += (ds[:, keys].T @ q_heads[h, rows]) * scale
+    return dk, dv

@@ -9,38 +9,14 @@ relative L2 error <= BWD_REL_L2 and max|err| <= BWD_MAX_REL * max|ref|.
 """
 from __future__ import annotations
 
-import numpy as np
 import pytest
 import torch
 
 import chiplet_numa_aware_amd as attn
 import oracle
-from chiplet_numa_aware_amd import inputs
-from tests.gpu_util import f64, say
+from tests.gpu_util import check_grad, f64, grad_inputs, say
 
 pytestmark = pytest.mark.gpu
-
-BWD_REL_L2 = 1e-2
-BWD_MAX_REL = 2e-2
-
-
-def grad_inputs(B, H_Q, H_KV, N, d, seed):
-    q, k, v = inputs.make_qkv(B, H_Q, H_KV, N, d, seed, "cuda")
-    dout = inputs.normal_bf16((B, H_Q, N, d), seed + 3, "cuda")
-    return q, k, v, dout
-
-
-def check_grad(got, ref, what):
-    got = np.asarray(got, np.float64)
-    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
-    denom = float(np.linalg.norm(ref))
-    err = got - ref
-    rel = float(np.linalg.norm(err)) / denom if denom > 0 else float(np.abs(err).max())
-    scale = float(np.abs(ref).max()) if ref.size else 0.0
-    mx = float(np.abs(err).max()) if err.size else 0.0
-    say(f"  {what}: relL2={rel:.3e} max|err|={mx:.3e} (max|ref| {scale:.3e})")
-    assert rel <= BWD_REL_L2, f"{what}: rel-L2 {rel}"
-    assert mx <= BWD_MAX_REL * max(scale, 1e-30), f"{what}: max|err| {mx} vs max|ref| {scale}"
 
 
 CASES = [

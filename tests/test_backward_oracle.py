@@ -161,3 +161,31 @@ def test_backward_pins_catch_mutant(name):
         except AssertionError:
             caught += 1
     assert caught > 0, f"no pin catches: {name}"
+
+
+# ---- sampled forms (long sequences) against the full oracle -----------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_forms_equal_full_backward(causal):
+    """dQ of chosen rows and dK/dV of chosen keys, computed one row or key
+    at a time, equal the full oracle on a GQA shape (2 query heads per KV
+    head), whatever the row chunk."""
+    rng = np.random.default_rng(11)
+    B, H_Q, H_KV, N, d = 1, 4, 2, 70, 16
+    q = rng.standard_normal((B, H_Q, N, d))
+    k = rng.standard_normal((B, H_KV, N, d))
+    v = rng.standard_normal((B, H_KV, N, d))
+    do = rng.standard_normal((B, H_Q, N, d))
+    dq, dk, dv = bwd_mod.attention_backward(q, k, v, do, causal)
+    rows = np.array([0, 1, 17, 68, 69])
+    for h in range(H_Q):
+        g = h // (H_Q // H_KV)
+        got = bwd_mod.backward_query_rows(q[0, h, rows], k[0, g], v[0, g], do[0, h, rows], rows, causal)
+        np.testing.assert_allclose(got, dq[0, h, rows], rtol=1e-12, atol=1e-12)
+    keys = np.array([0, 5, 33, 69])
+    for g in range(H_KV):
+        heads = [g * 2, g * 2 + 1]
+        for chunk in (7, 512):
+            gk, gv = bwd_mod.backward_key_rows(q[0, heads], k[0, g], v[0, g], do[0, heads], keys,
+                                               causal, row_chunk=chunk)
+            np.testing.assert_allclose(gk, dk[0, g, keys], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(gv, dv[0, g, keys], rtol=1e-12, atol=1e-12)
