@@ -13,6 +13,8 @@ Head-first.  Prints ONE JSON line on stdout (progress goes to stderr).
   python bench.py --sweep OUT.md    every configuration x mapping mode, timed
   python bench.py --pass bwd [--workload NAME]   the backward pass (attn_bwd):
                   dQ, dK, dV from the forward's O and lse, one JSON line
+  python bench.py --pass gemm [--workload NAME]  the CAC-scheduled GEMM
+                  (cac_gemm) per tile map, with torch.mm as context
 """
 from __future__ import annotations
 
@@ -36,7 +38,22 @@ KERNEL_SOURCES = {
 }
 # Kernels whose counters a profile reports, per pass.
 PASS_KERNELS = {"fwd": ["attn_fwd_kernel"],
-                "bwd": ["attn_bwd_dkv_kernel", "attn_bwd_dq_kernel"]}
+                "bwd": ["attn_bwd_dkv_kernel", "attn_bwd_dq_kernel"],
+                "gemm": ["cac_gemm_kernel"]}
+KERNEL_SOURCES["gemm"] = ["chiplet_numa_aware_amd/csrc/gemm_kernel.hpp",
+                          "chiplet_numa_aware_amd/csrc/cac_map.hpp",
+                          "chiplet_numa_aware_amd/csrc/attn_fwd_kernel.hpp",
+                          "chiplet_numa_aware_amd/csrc/cac_gemm.hip"]
+GEMM_METRIC = "CAC-scheduled bf16 GEMM TFLOP/s + % bf16 MFMA peak + L2 hit % per tile map"
+GEMM_MODE_NAMES = ["naive_row_major", "naive_cluster", "swizzled_row_major", "swizzled_cluster"]
+GEMM_WORKLOADS = {
+    # name: (L, M, N, K); C = A B^T with A [L,M,K], B [L,N,K]
+    # 8 tile columns: the dispatcher's round robin gives each XCD one column.
+    "gemm_tall_64k_2k_8k": (1, 65536, 2048, 8192),
+    "gemm_sq_16k": (1, 16384, 16384, 16384),
+    # 4 tile columns, batched (per-batch B panels shared by the batch's tiles)
+    "gemm_b8_16k_1k_4k": (8, 16384, 1024, 4096),
+}
 BWD_METRIC = "attn bwd TFLOP/s (dQ, dK, dV; 2.5x the forward's FLOPs) + % bf16 MFMA peak + L2 hit %"
 
 METRIC = "attn fwd TFLOP/s + % bf16 MFMA peak + L2 hit %, MHA H=128 N=128K d=128"
@@ -262,8 +279,8 @@ PROFILE_PASSES = {
 def profile_commands(workload: str, out: str, which: str = "fwd"):
     """The rocprofv3 runs whose output --summarize-profile reads."""
     bench = "python3 /root/repo/bench.py"
-    modes = ",".join(map(str, PROFILE_MODES))
-    sel = f"--workload {workload}" + (" --pass bwd" if which == "bwd" else "")
+    modes = "0,1,2,3" if which == "gemm" else ",".join(map(str, PROFILE_MODES))
+    sel = f"--workload {workload}" + ("" if which == "fwd" else f" --pass {which}")
     one = f"{bench} {sel} --steps 1 --warmup 0 --modes {modes} --no-cpu-baseline"
     cmds = {"trace": (f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/trace -o trace -- "
                       f"{bench} {sel} --steps 2 --warmup 1 --modes {modes} --no-cpu-baseline")}
@@ -572,6 +589,163 @@ def run_bwd(args, attn, inputs):
     print(json.dumps(out), flush=True)
 
 
+def gemm_describe(name) -> str:
+    L, M, N, K = GEMM_WORKLOADS[name]
+    return f"GEMM C = A B^T, L={L} M={M} N={N} K={K} bf16"
+
+
+def run_gemm(args, attn, inputs):
+    """--pass gemm: times cac_gemm per tile map (and torch.mm on the same
+    operands as context); prints one JSON line."""
+    import torch
+    L, M, N, K = GEMM_WORKLOADS[args.workload]
+    modes = [int(m) for m in args.modes.split(",") if m.strip() != ""]
+    flops = 2.0 * L * M * N * K
+    log(f"workload {gemm_describe(args.workload)}: {flops / 1e12:.2f} TFLOP per call")
+    a = inputs.normal_bf16((L, M, K), 1000, "cuda")
+    b = inputs.normal_bf16((L, N, K), 1001, "cuda")
+    c = torch.empty((L, M, N), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    results = {}
+    for mode in modes:
+        log(f"  timing cac_gemm mapping {mode} ({GEMM_MODE_NAMES[mode]})")
+
+        def call(stream, mode=mode):
+            attn.cac_gemm(a, b, mapping=mode, c=c, stream=stream)
+        r = time_calls(call, args.steps, args.warmup, flops)
+        results[mode] = r
+        log(f"  {GEMM_MODE_NAMES[mode]:20s} {r['kernel_tflops']:8.1f} TFLOP/s "
+            f"({r['pct_peak']:.1f}% of peak, {r['kernel_ms_avg']:.3f} ms)")
+    # Context: the vendor library on the same operands, one plain 2-D GEMM per
+    # batch (torch.mm of A[l] and the transposed view of B[l]); batched bf16
+    # products with a transposed right operand are avoided on purpose.
+    log("  timing torch.mm per batch (hipBLASLt)")
+
+    def library(stream):
+        for l in range(L):
+            torch.mm(a[l], b[l].t(), out=c[l])
+    ref = time_calls(library, args.steps, args.warmup, flops)
+    log(f"  torch.mm (hipBLASLt)      {ref['kernel_tflops']:8.1f} TFLOP/s")
+    headline = 3 if 3 in modes else modes[-1]
+    counters = stored_counters(args.workload, kernel_hash("gemm"), "gemm")
+    head = results[headline]
+    modes_out = {}
+    for mode, r in results.items():
+        entry = {k2: round(v2, 4) for k2, v2 in r.items()}
+        if counters and GEMM_MODE_NAMES[mode] in counters["modes"]:
+            entry["l2_hit_pct"] = counters["modes"][GEMM_MODE_NAMES[mode]]["l2_hit_pct"]
+        modes_out[GEMM_MODE_NAMES[mode]] = entry
+    traffic = None
+    if counters and GEMM_MODE_NAMES[headline] in counters["modes"]:
+        cm = counters["modes"][GEMM_MODE_NAMES[headline]]
+        traffic = cm["fetch_bytes"] + cm["write_bytes"]
+    out = {
+        "metric": GEMM_METRIC,
+        "value": round(head["kernel_tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: bf16 N(0,1) A/B from fixed seeds",
+        "config": {"workload": gemm_describe(args.workload), "L": L, "M": M, "N": N, "K": K,
+                   "mapping": GEMM_MODE_NAMES[headline], "cluster": "4 x 8 tiles of 256 x 256",
+                   "parallelism": "single GPU"},
+        "pct_peak": round(head["pct_peak"], 2),
+        "modes": modes_out,
+        "torch_mm_tflops": round(ref["kernel_tflops"], 2),
+        "roofline": {"bound": "mfma", "achieved": round(head["kernel_tflops"], 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(head["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "kernel_hash": kernel_hash("gemm"),
+    }
+    if 0 in results and headline != 0:
+        out["speedup_vs_naive_row_major"] = round(results[0]["kernel_ms_avg"] / head["kernel_ms_avg"], 4)
+    print(json.dumps(out), flush=True)
+
+
+def summarize_gemm_profile(directory: str, workload: str):
+    """rocprofv3 CSVs of profile_commands(..., "gemm") into
+    profiles/cac_gemm_<workload>.md and counters_gemm_<workload>.json."""
+    import csv
+    import glob
+    L, M, N, K = GEMM_WORKLOADS[workload]
+    flops = 2.0 * L * M * N * K
+
+    def one(pass_name, kernel):
+        files = glob.glob(os.path.join(directory, pass_name, "*_counter_collection.csv"))
+        if not files:
+            raise SystemExit(f"missing {pass_name} counters under {directory}")
+        return _read_counters(files[0], kernel)
+
+    cal = {}
+    for name, ctr in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        v, _ = one("copy_" + name, "copyBuffer")
+        cal[ctr] = (1 << 30) / (v[-1][ctr] * 1024.0)
+    l2, durs = one("l2", "cac_gemm_kernel")
+    fe, _ = one("fetch", "cac_gemm_kernel")
+    wr, _ = one("write", "cac_gemm_kernel")
+    mf, mdur = one("mfma", "cac_gemm_kernel")
+    if not (len(l2) == len(fe) == len(wr) == len(mf) == 4):
+        raise SystemExit("expected one cac_gemm dispatch per tile map in every pass")
+    unique = 2 * L * (M * K + N * K + M * N)
+    modes = {}
+    for m in range(4):
+        hit, miss = l2[m]["TCC_HIT_sum"], l2[m]["TCC_MISS_sum"]
+        fetch_b = fe[m]["FETCH_SIZE"] * 1024.0 * cal["FETCH_SIZE"]
+        write_b = wr[m]["WRITE_SIZE"] * 1024.0 * cal["WRITE_SIZE"]
+        gui = mf[m]["GRBM_GUI_ACTIVE"]
+        modes[GEMM_MODE_NAMES[m]] = {
+            "l2_hit_pct": round(100.0 * hit / (hit + miss), 2),
+            "fetch_bytes": fetch_b, "write_bytes": write_b,
+            "fetch_over_unique": round(fetch_b / unique, 2),
+            "mfma_busy_pct": round(100.0 * mf[m]["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui / 8.0 * 1024), 2),
+            "clock_ghz": round(gui / 8.0 / mdur[m] / 1e9, 3),
+            "kernel_ms_counter_run": round(durs[m] * 1e3, 3),
+            "tflops_counter_run": round(flops / durs[m] / 1e12, 1),
+        }
+    trace = glob.glob(os.path.join(directory, "trace", "*_kernel_stats.csv"))
+    stats = []
+    if trace:
+        with open(trace[0]) as f:
+            stats = [r for r in csv.DictReader(f)]
+    data = {"kernel": "attn_numa::cac_gemm_kernel", "kernel_hash": kernel_hash("gemm"),
+            "workload": workload, "description": gemm_describe(workload),
+            "algorithmic_flops": flops, "unique_bytes": unique,
+            "calibration": {"copy_bytes": 1 << 30, "scale": cal}, "modes": modes,
+            "commands": _recorded_commands(directory, workload, "gemm")}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"counters_gemm_{workload}.json"), "w") as f:
+        json.dump(data, f, indent=1)
+    lines = [f"# cac_gemm_kernel, {gemm_describe(workload)}", "",
+             f"Kernel source hash {data['kernel_hash']} (sha256 of the GEMM's sources, first 16 hex).",
+             f"Algorithmic work {flops / 1e12:.2f} TFLOP per call; unique A+B+C "
+             f"{unique / 2**30:.2f} GiB.", "", "## rocprofv3 --kernel-trace --stats", "",
+             "| kernel | calls | average ms | min ms | max ms |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {r['Name'].split('(')[0]} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
+                     f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} |")
+    lines += ["", "(the trace mixes the 4 tile maps, 3 calls each, and torch.mm's kernels)", "",
+              "## Counters per tile map (one dispatch each)", "",
+              "| tile map | L2 hit % | HBM read GB | HBM write GB | read / unique | MFMA busy % | clock GHz | ms | TFLOP/s |",
+              "|---|---|---|---|---|---|---|---|---|"]
+    for name, mm in modes.items():
+        lines.append(f"| {name} | {mm['l2_hit_pct']} | {mm['fetch_bytes'] / 1e9:.2f} | "
+                     f"{mm['write_bytes'] / 1e9:.2f} | {mm['fetch_over_unique']} | {mm['mfma_busy_pct']} | "
+                     f"{mm['clock_ghz']} | {mm['kernel_ms_counter_run']} | {mm['tflops_counter_run']} |")
+    lines += ["", f"HBM bytes: FETCH_SIZE and WRITE_SIZE scaled by a plain 1 GiB copy's counts "
+              f"(read x{cal['FETCH_SIZE']:.3f}, write x{cal['WRITE_SIZE']:.3f}).", "", "## Commands", "",
+              "Each pass is its own process, run as `cd /tmp && export TMPDIR=/tmp && <command>` "
+              "with the repository at /root/repo; then "
+              f"`python3 bench.py --workload {workload} --pass gemm --summarize-profile DIR` wrote this file.", ""]
+    for name, cmd in data["commands"].items():
+        lines.append(f"- {name}: `{cmd}`")
+    with open(os.path.join(PROFILES, f"cac_gemm_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({k: v for k, v in data.items() if k != "commands"}, indent=1))
+
+
 def run_sweep(out_path: str):
     """Times every SWEEP configuration under the four mapping modes (2 warmup
     calls, then the median of 5 calls, 10 when N <= 32K) and writes a table."""
@@ -667,12 +841,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="mha_128k", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=None,
+                    choices=sorted(WORKLOADS) + sorted(GEMM_WORKLOADS),
+                    help="default: mha_128k (gemm_tall_64k_2k_8k for --pass gemm)")
     ap.add_argument("--modes", default="0,1,2,3",
                     help="mapping modes to time; the last one listed that is "
                          "3 (or the last one) is the headline")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
-                    help="fwd: attn_fwd (default); bwd: attn_bwd on the forward's O, lse")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "gemm"), default="fwd",
+                    help="fwd: attn_fwd (default); bwd: attn_bwd on the forward's O, lse; "
+                         "gemm: cac_gemm (workloads gemm_*)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--sweep", metavar="OUT_MD",
@@ -686,8 +863,14 @@ def main():
     ap.add_argument("--print-profile-commands", metavar="OUT",
                     help="print the rocprofv3 commands for --workload, output under OUT")
     args = ap.parse_args()
+    if args.workload is None:
+        args.workload = "gemm_tall_64k_2k_8k" if args.which == "gemm" else "mha_128k"
+    if (args.which == "gemm") != (args.workload in GEMM_WORKLOADS):
+        ap.error("--pass gemm takes a gemm_* workload; the attention passes take the others")
     if args.summarize_profile:
-        if args.which == "bwd":
+        if args.which == "gemm":
+            summarize_gemm_profile(args.summarize_profile, args.workload)
+        elif args.which == "bwd":
             summarize_bwd_profile(args.summarize_profile, args.workload)
         else:
             summarize_profile(args.summarize_profile, args.workload)
@@ -726,6 +909,9 @@ def main():
         return
     if args.which == "bwd":
         run_bwd(args, attn, inputs)
+        return
+    if args.which == "gemm":
+        run_gemm(args, attn, inputs)
         return
     B, H_Q, H_KV, N, d, causal = WORKLOADS[args.workload]
     modes = [int(m) for m in args.modes.split(",") if m.strip() != ""]

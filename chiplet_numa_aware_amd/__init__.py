@@ -10,6 +10,9 @@ entry points have the names of the C ABI in include/attn_numa.h:
 * ``attn_split_chunk(N_kv, num_splits)``
 * ``attn_merge(o_parts, lse_parts, o=None, lse=None)``
 * ``attn_bwd(q, k, v, o, dout, lse, causal=False, mapping=3, ...)``
+* ``cac_gemm(a, b, mapping=3, group_m=0, group_n=0, c=None)`` (include/cac_gemm.h)
+* ``cac_gemm_map(mapping, L, M, N, group_m, group_n, num_xcd)``
+* ``cac_gemm_tile()``
 * ``attn_wg_map(mapping, B, H_Q, H_KV, N, num_xcd)``
 * ``attn_num_xcd()``
 * ``attn_block_m()``
@@ -29,6 +32,7 @@ import torch  # first, so the library binds to the HIP runtime torch loaded
 
 __all__ = [
     "AttnError", "attn_fwd", "attn_fwd_split", "attn_split_chunk", "attn_merge", "attn_bwd",
+    "cac_gemm", "cac_gemm_map", "cac_gemm_tile", "CAC_MAPPINGS",
     "attn_wg_map", "attn_num_xcd", "attn_block_m",
     "attn_probe_placement", "attn_strerror", "library_path", "load_library",
     "MAPPINGS", "row_blocks", "num_workgroups", "BLOCK_M",
@@ -43,6 +47,14 @@ MAPPINGS = {
     "naive_head_first": 1,
     "swizzled_block_first": 2,
     "swizzled_head_first": 3,
+}
+
+# Tile map modes of cac_gemm (CAC_MAP_* in include/cac_gemm.h).
+CAC_MAPPINGS = {
+    "naive_row_major": 0,
+    "naive_cluster": 1,
+    "swizzled_row_major": 2,
+    "swizzled_cluster": 3,
 }
 
 _lib = None
@@ -78,6 +90,12 @@ def load_library():
     lib.attn_merge.restype = i32
     lib.attn_bwd.argtypes = [vp] * 10 + [i32] * 7 + [vp]
     lib.attn_bwd.restype = i32
+    lib.cac_gemm.argtypes = [vp, vp, vp] + [i32] * 7 + [vp]
+    lib.cac_gemm.restype = i32
+    lib.cac_gemm_tile.argtypes = []
+    lib.cac_gemm_tile.restype = i32
+    lib.cac_gemm_map.argtypes = [i32] * 7 + [vp]
+    lib.cac_gemm_map.restype = i32
     lib.attn_wg_map.argtypes = [i32] * 6 + [vp]
     lib.attn_wg_map.restype = i32
     lib.attn_num_xcd.argtypes = []
@@ -303,6 +321,62 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                           _stream_handle(stream, q.device))
     _check(rc, "attn_bwd")
     return dq, dk, dv
+
+
+def cac_gemm_tile() -> int:
+    """Rows and columns of one C tile of cac_gemm (host, no GPU)."""
+    return int(load_library().cac_gemm_tile())
+
+
+def _cac_mapping_id(mapping) -> int:
+    if isinstance(mapping, str):
+        return CAC_MAPPINGS[mapping]
+    return int(mapping)
+
+
+def cac_gemm(a: torch.Tensor, b: torch.Tensor, mapping=3, group_m: int = 0,
+             group_n: int = 0, c: torch.Tensor | None = None,
+             stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """C = A B^T (per batch) on the GPU.  a [L,M,K] or [M,K], b [L,N,K] or
+    [N,K], contiguous bf16; returns c [L,M,N] (or [M,N]) bf16, allocated when
+    not given.  ``mapping`` is the Compute Affinity Cluster tile map
+    (CAC_MAPPINGS), group_m x group_n the cluster in 256 x 256 tiles (0: the
+    library default).  Enqueued on ``stream``; returns without synchronising."""
+    squeeze = a.dim() == 2
+    a3 = a.unsqueeze(0) if squeeze else a
+    b3 = b.unsqueeze(0) if b.dim() == 2 else b
+    for name, t in (("a", a3), ("b", b3)):
+        if t.dim() != 3 or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 GPU tensor [L, rows, K]")
+    L, M, K = a3.shape
+    if b3.shape[0] != L or b3.shape[2] != K:
+        raise ValueError("b must be [L, N, K] with a's L and K")
+    N = b3.shape[1]
+    shape = (M, N) if squeeze else (L, M, N)
+    if c is None:
+        c = torch.empty(shape, dtype=torch.bfloat16, device=a.device)
+    elif (tuple(c.shape) != shape or c.dtype != torch.bfloat16 or not c.is_contiguous()):
+        raise ValueError(f"c must be a contiguous bf16 tensor of shape {shape}")
+    lib = load_library()
+    with torch.cuda.device(a.device):
+        rc = lib.cac_gemm(a3.data_ptr(), b3.data_ptr(), c.data_ptr(), L, M, N, K,
+                          _cac_mapping_id(mapping), int(group_m), int(group_n),
+                          _stream_handle(stream, a.device))
+    _check(rc, "cac_gemm")
+    return c
+
+
+def cac_gemm_map(mapping, L: int, M: int, N: int, group_m: int = 0, group_n: int = 0,
+                 num_xcd: int = 8) -> np.ndarray:
+    """(l, tile row, tile column) of every workgroup id of cac_gemm, int32
+    [W, 3] (host, no GPU)."""
+    t = cac_gemm_tile()
+    W = L * (-(-M // t)) * (-(-N // t))
+    out = np.empty((max(W, 1), 3), dtype=np.int32)
+    rc = load_library().cac_gemm_map(_cac_mapping_id(mapping), L, M, N, int(group_m),
+                                     int(group_n), num_xcd, out.ctypes.data)
+    _check(rc, "cac_gemm_map")
+    return out[:W]
 
 
 def attn_wg_map(mapping, B: int, H_Q: int, H_KV: int, N: int,

@@ -1,0 +1,167 @@
+// Tiled bf16 GEMM for gfx950 whose workgroup -> tile placement is the
+// Compute Affinity Cluster map (cac_map.hpp).
+//
+// C[l] = A[l] B[l]^T for l < L, with A [L][M][K], B [L][N][K] and C [L][M][N]
+// row-major bf16 (both operands K-contiguous, the layout of the attention's
+// S = Q K^T), fp32 accumulation, C rounded to bf16 (nearest-even).
+//
+// One workgroup computes one 256 x 256 tile of C with 4 waves; wave w owns
+// rows 128 (w / 2) .. +128 and columns 128 (w % 2) .. +128 as 4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16.  Each block is computed transposed,
+// C^T = B A^T (A operand: 32 columns of B; B operand: 32 rows of A), so a
+// lane's 16 accumulators are 4 runs of 4 consecutive columns of one C row and
+// the epilogue writes 8-byte pieces.  K advances 32 at a time; the A and B
+// slices of a K step go from global memory straight into LDS (buffer loads
+// with the LDS-direct bit), four stages deep, so a step's loads have two
+// steps of MFMAs to land.  An LDS slice is 256 rows of four 16-byte chunks;
+// chunk c of row r sits at slot c ^ ((r >> 1) & 3), which keeps the 16-byte
+// operand reads free of bank conflicts.  Rows past M or N read as zero
+// (range-checked buffer offsets), K chunks past K use an offset that is
+// always out of range, and stores outside C are dropped.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_fwd_kernel.hpp"
+#include "cac_map.hpp"
+
+namespace attn_numa {
+
+constexpr int kGemmTile = 256;   // rows and columns of a C tile
+constexpr int kGemmBK = 32;      // K per step
+constexpr int kGemmStages = 4;   // LDS stages (a power of 2)
+constexpr int kGemmThreads = 256;
+constexpr int kGemmRowB = kGemmBK * 2;              // bytes of one LDS row
+constexpr int kGemmSliceB = kGemmTile * kGemmRowB;  // one operand's K slice (16 KiB)
+constexpr int kGemmStageB = 2 * kGemmSliceB;        // A slice, then B slice
+constexpr int kGemmLoads = kGemmSliceB / 16 / kGemmThreads;  // 16-byte loads per thread per slice
+static_assert(kGemmLoads * 16 * kGemmThreads == kGemmSliceB, "a slice splits into the workgroup");
+
+__global__ __launch_bounds__(kGemmThreads, 1) void cac_gemm_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, uint16_t* __restrict__ c,
+    int L, int M, int N, int K, int Mt, int Nt, int mapping, int gm, int gn, int num_xcd) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kGemmStages * kGemmStageB / 4];
+  char* const lb = reinterpret_cast<char*>(lds);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lb);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const TileCoord tc = cac_tile_map(mapping, blockIdx.x, L, Mt, Nt, gm, gn, num_xcd);
+  const int m0 = (int)tc.tm * kGemmTile, n0 = (int)tc.tn * kGemmTile;
+  const uint32_t a_bytes = (uint32_t)M * (uint32_t)K * 2u;
+  const uint32_t b_bytes = (uint32_t)N * (uint32_t)K * 2u;
+  const uint32_t c_bytes = (uint32_t)M * (uint32_t)N * 2u;
+  const u32x4 a_desc = make_desc(a + (uint64_t)tc.l * M * K, a_bytes);
+  const u32x4 b_desc = make_desc(b + (uint64_t)tc.l * N * K, b_bytes);
+
+  // Tile loads: instruction i of this thread fills LDS slot P = tid + 256 i of
+  // a slice (row P / 4, slot P % 4 holding chunk (P % 4) ^ ((row >> 1) & 3)).
+  // The row offset of the tile goes in soffset (capped at the buffer size, so
+  // rows past the matrix read zero); voffset is the row within the tile and
+  // the K position.
+  const uint32_t a_soff = min((uint32_t)m0 * (uint32_t)K * 2u, a_bytes);
+  const uint32_t b_soff = min((uint32_t)n0 * (uint32_t)K * 2u, b_bytes);
+  uint32_t ld_row[kGemmLoads];
+  int ld_k[kGemmLoads];
+#pragma unroll
+  for (int i = 0; i < kGemmLoads; ++i) {
+    const int P = tid + kGemmThreads * i;
+    const int row = P >> 2;
+    const int chunk = (P & 3) ^ ((row >> 1) & 3);
+    ld_row[i] = (uint32_t)row * (uint32_t)K * 2u;
+    ld_k[i] = chunk * 8;
+  }
+  const int n_steps = (K + kGemmBK - 1) / kGemmBK;
+  auto issue = [&](int step) {
+    const int st = step & (kGemmStages - 1);
+    const int k0 = step * kGemmBK;
+#pragma unroll
+    for (int i = 0; i < kGemmLoads; ++i) {
+      const int kk = k0 + ld_k[i];
+      const uint32_t voff = kk < K ? ld_row[i] + (uint32_t)kk * 2u : kOutOfRange;
+      const uint32_t m0b = lds_base + st * kGemmStageB + (wave + 4 * i) * 1024;
+      load_lds(a_desc, voff, a_soff, m0b);
+      load_lds(b_desc, voff, b_soff, m0b + kGemmSliceB);
+    }
+  };
+
+  // Operand reads: lane (row l32 of a 32-row block, half g) reads chunk
+  // 2 kc + g of its row.
+  int rd[2];
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) rd[kc] = l32 * kGemmRowB + (((2 * kc + g) ^ ((l32 >> 1) & 3)) * 16);
+  const int wm = 128 * (wave >> 1), wn = 128 * (wave & 1);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  // Prologue: steps 0 .. stages-2 in flight.
+#pragma unroll
+  for (int s = 0; s < kGemmStages - 1; ++s)
+    if (s < n_steps) issue(s);
+  for (int step = 0; step < n_steps; ++step) {
+    // Step `step` has landed when at most the loads of the (up to two) later
+    // steps already issued are outstanding (loads retire in order).
+    const int later = min(n_steps - 1 - step, kGemmStages - 2);
+    if (later >= 2)
+      wait_vmcnt<4 * kGemmLoads>();
+    else if (later == 1)
+      wait_vmcnt<2 * kGemmLoads>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    // All 16 operand fragments of the step first (two 16-deep K chunks),
+    // then the loads of a later step, then the 32 MFMAs: the MFMAs of chunk 0
+    // wait only for its own fragments, and chunk 1's arrive meanwhile.
+    const char* sa = lb + (step & (kGemmStages - 1)) * kGemmStageB;
+    const char* sb = sa + kGemmSliceB;
+    bf16x8 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa[kc][i] = *reinterpret_cast<const bf16x8*>(sa + (wm + 32 * i) * kGemmRowB + rd[kc]);
+        fb[kc][i] = *reinterpret_cast<const bf16x8*>(sb + (wn + 32 * i) * kGemmRowB + rd[kc]);
+      }
+    // The stage written next was last read in step - 1, which every wave
+    // finished before the barrier above.
+    if (step + kGemmStages - 1 < n_steps) issue(step + kGemmStages - 1);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kc][j], fa[kc][i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // the 16 LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);  // then the 32 MFMAs
+  }
+
+  // acc[i][j] register r: C row m0 + wm + 32 i + l32, column
+  // n0 + wn + 32 j + 8 (r / 4) + 4 g + (r % 4).
+  const __amdgpu_buffer_rsrc_t c_rs = make_rsrc(c + (uint64_t)tc.l * M * N, c_bytes);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + wm + 32 * i + l32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int col = n0 + wn + 32 * j + 8 * rr + 4 * g;
+        if (row < M && col < N) {
+          u32x2 w;
+          w.x = pack_bf16x2(acc[i][j][4 * rr + 0], acc[i][j][4 * rr + 1]);
+          w.y = pack_bf16x2(acc[i][j][4 * rr + 2], acc[i][j][4 * rr + 3]);
+          __builtin_amdgcn_raw_buffer_store_b64(w, c_rs, ((uint32_t)row * (uint32_t)N + col) * 2u, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace attn_numa

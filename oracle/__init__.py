@@ -1,4 +1,5 @@
-"""CPU oracle for the NUMA-aware attention forward pass (test infrastructure).
+"""CPU oracle for the NUMA-aware attention and the CAC-scheduled GEMM (test
+infrastructure).
 
 Only tests/, ``__graft_entry__.smoke()`` and bench.py's cpu_baseline leg may
 import this package.  It shares no code with the HIP path.
@@ -6,6 +7,7 @@ import this package.  It shares no code with the HIP path.
 from .sdpa import attention, attention_head_rows, attention_sampled, kv_head
 from .split import causal_offset, merge, partial_attention, partial_head_rows
 from .backward import attention_backward, backward_key_rows, backward_query_rows
+from .gemm import cac_tile_table, gemm
 from .remap import (NBF, NHF, SBF, SHF, LONGEST_FIRST, MODE_NAMES, chiplet_swizzle,
                      num_workgroups, row_blocks, wg_map, wg_table, xcd_of)
 
@@ -13,6 +15,7 @@ __all__ = [
     "attention", "attention_head_rows", "attention_sampled", "kv_head",
     "causal_offset", "merge", "partial_attention", "partial_head_rows",
     "attention_backward", "backward_key_rows", "backward_query_rows",
+    "cac_tile_table", "gemm",
     "NBF", "NHF", "SBF", "SHF", "LONGEST_FIRST", "MODE_NAMES", "chiplet_swizzle",
     "num_workgroups", "row_blocks", "wg_map", "wg_table", "xcd_of",
 ]

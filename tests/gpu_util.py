@@ -89,3 +89,27 @@ def grad_inputs(B, H_Q, H_KV, N, d, seed):
     q, k, v = inputs.make_qkv(B, H_Q, H_KV, N, d, seed, "cuda")
     dout = inputs.normal_bf16((B, H_Q, N, d), seed + 3, "cuda")
     return q, k, v, dout
+
+
+def check_gemm(c_gpu, a, b, what=""):
+    """Elementwise bound for C = A B^T with bf16 inputs, fp32 accumulation and
+    a bf16 result: the fp32 sum of K exact products is within
+    gamma_K * sum_k |a_ik b_jk| of the exact value (gamma_K = K u / (1 - K u),
+    u = 2^-24, any summation order), and rounding it to bf16 adds at most half
+    a bf16 ulp of its magnitude."""
+    import oracle
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    ref = oracle.gemm(a, b)
+    K = a.shape[-1]
+    u = 2.0 ** -24
+    gamma = K * u / (1 - K * u)
+    s = oracle.gemm(np.abs(a), np.abs(b))
+    bound = half_ulp_bf16(np.abs(ref) + gamma * s) + gamma * s
+    got = np.asarray(c_gpu, np.float64)
+    err = np.abs(got - ref)
+    worst = float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    say(f"  {what}: max err/bound={worst:.3f} relL2={rel:.3e}")
+    assert np.all(np.isfinite(got)), f"{what}: non-finite C"
+    assert np.all(err <= bound), f"{what}: error above the bound (worst ratio {worst})"

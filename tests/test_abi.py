@@ -225,3 +225,57 @@ def test_bwd_argument_errors(lib):
     assert b(mapping=-1) == c["ATTN_E_MAPPING"]
     for n in ("q", "dout", "lse", "dk", "ws"):
         assert b(mapping_ok=1, **{n: FAKE + 4}) == c["ATTN_E_ALIGN"], n
+
+
+GEMM_HEADER = os.path.join(os.path.dirname(HEADER), "cac_gemm.h")
+
+
+def test_gemm_header_symbols_exported(lib):
+    text = re.sub(r"/\*.*?\*/", "", open(GEMM_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(cac_\w+)\s*\(", text)))
+    assert set(names) == {"cac_gemm", "cac_gemm_tile", "cac_gemm_map"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.cac_gemm_tile() == 256
+
+
+def test_gemm_host_map_equals_oracle():
+    import oracle
+    t = attn.cac_gemm_tile()
+    for mode in range(4):
+        for L, M, N, g1, g2, X in [(1, 3 * t, 5 * t, 2, 2, 8), (2, 7 * t - 5, 3 * t, 4, 3, 8),
+                                   (1, 64 * t, 8 * t, 0, 0, 8), (3, 5 * t, 5 * t - 8, 2, 3, 3),
+                                   (1, 100, 40, 0, 0, 8), (2, 9 * t, 11 * t, 0, 0, 5)]:
+            Mt, Nt = -(-M // t), -(-N // t)
+            gm_ = min(g1 or 4, Mt)
+            gn_ = min(g2 or 8, Nt)
+            want = oracle.cac_tile_table(mode, L, Mt, Nt, gm_, gn_, X)
+            got = attn.cac_gemm_map(mode, L, M, N, g1, g2, X)
+            assert np.array_equal(got, want), (mode, L, M, N, g1, g2, X)
+
+
+def test_gemm_argument_errors(lib):
+    """Rejected before anything could launch on the fake pointers."""
+    c = _declared_codes()
+
+    def g(**kw):
+        return lib.cac_gemm(kw.get("a", FAKE), kw.get("b", FAKE), kw.get("c", FAKE),
+                            kw.get("L", 1), kw.get("M", 300), kw.get("N", 136), kw.get("K", 72),
+                            kw.get("mapping", 4 if "mapping_ok" not in kw else 3),
+                            kw.get("gm", 0), kw.get("gn", 0), None)
+
+    for n in ("a", "b", "c"):
+        assert g(**{n: None}) == c["ATTN_E_NULL"], n
+    for kw in ({"L": 0}, {"M": 0}, {"N": 0}, {"K": 0}, {"N": 100}, {"K": 12},
+               {"K": (1 << 20) + 8}, {"M": 1 << 20, "K": 2048}, {"N": 1 << 20, "K": 2048},
+               {"M": 1 << 17, "N": 1 << 14}, {"L": 1 << 24, "M": 1 << 12, "N": 1 << 12},
+               {"gm": -1, "mapping_ok": 1}, {"gn": -2, "mapping_ok": 1}):
+        assert g(**kw) == c["ATTN_E_SHAPE"], kw
+    assert g() == c["ATTN_E_MAPPING"]          # mapping 4
+    assert g(mapping=-1) == c["ATTN_E_MAPPING"]
+    for n in ("a", "b", "c"):
+        assert g(mapping_ok=1, **{n: FAKE + 8}) == c["ATTN_E_ALIGN"], n
+    out = np.empty((4, 3), dtype=np.int32)
+    assert lib.cac_gemm_map(3, 1, 256, 256, 0, 0, 0, out.ctypes.data) == c["ATTN_E_SHAPE"]
+    assert lib.cac_gemm_map(4, 1, 256, 256, 0, 0, 8, out.ctypes.data) == c["ATTN_E_MAPPING"]
+    assert lib.cac_gemm_map(3, 1, 256, 256, 0, 0, 8, None) == c["ATTN_E_NULL"]
