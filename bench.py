@@ -30,7 +30,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "fwd": ["chiplet_numa_aware_amd/csrc/attn_fwd_kernel.hpp",
             "chiplet_numa_aware_amd/csrc/wg_map.hpp",
-            "chiplet_numa_aware_amd/csrc/attn_numa.hip"],
+            "chiplet_numa_aware_amd/csrc/fwd_launch.hpp",
+            "chiplet_numa_aware_amd/csrc/attn_fwd_d64.hip",
+            "chiplet_numa_aware_amd/csrc/attn_fwd_d128.hip",
+            "chiplet_numa_aware_amd/csrc/attn_fwd.hip"],
     "bwd": ["chiplet_numa_aware_amd/csrc/attn_bwd_kernel.hpp",
             "chiplet_numa_aware_amd/csrc/attn_fwd_kernel.hpp",
             "chiplet_numa_aware_amd/csrc/wg_map.hpp",

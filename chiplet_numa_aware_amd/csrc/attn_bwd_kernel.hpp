@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_fwd_kernel.hpp"
 #include "wg_map.hpp"
 
@@ -75,28 +77,34 @@ struct BwdCfg {
 };
 
 // Per-lane LDS addresses of the two operand kinds, for a tile at byte 0.
+// The swizzle XORs the low three bits of the chunk index only, so chunks
+// 8..15 of a row sit 128 bytes after chunks 0..7: only the first eight
+// chunks' addresses are kept, and the rest become instruction offsets.
 template <int D>
 struct TileAddr {
   using C = BwdCfg<D>;
-  int row_addr[C::KC];  // 16-byte read of row l32, chunk 2kc + g
-  int tr_addr[C::DB];   // transposing read (4 rows x 8 bytes per lane group)
+  static constexpr int NR = C::KC < 4 ? C::KC : 4, NT = C::DB < 2 ? C::DB : 2;
+  int row_addr[NR];  // 16-byte read of row l32, chunk 2kc + g
+  int tr_addr[NT];   // transposing read (4 rows x 8 bytes per lane group)
   __device__ __forceinline__ TileAddr(int lane) {
     const int g = lane >> 5, l32 = lane & 31;
 #pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc)
+    for (int kc = 0; kc < NR; ++kc)
       row_addr[kc] = l32 * C::ROWB + (((kc * 2 + g) ^ (l32 & 7)) * 16);
     const int j = lane & 15, kk = j >> 2, qq = j & 3, dhalf = (lane >> 4) & 1;
     const int krow = 4 * g + kk, w = 2 * dhalf + (qq >> 1);
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < NT; ++db)
       tr_addr[db] = krow * C::ROWB + (((4 * db + w) ^ krow) * 16) + (qq & 1) * 8;
   }
+  __device__ __forceinline__ int row(int kc) const { return row_addr[kc % NR] + (kc / NR) * 128; }
+  __device__ __forceinline__ int tr(int db) const { return tr_addr[db % NT] + (db / NT) * 128; }
 };
 
 template <int D>
 __device__ __forceinline__ bf16x8 lds_row_frag(const char* lds, int tile_byte,
                                                const TileAddr<D>& a, int kc) {
-  return *reinterpret_cast<const bf16x8*>(lds + tile_byte + a.row_addr[kc]);
+  return *reinterpret_cast<const bf16x8*>(lds + tile_byte + a.row(kc));
 }
 // Rows 16c .. 16c+15 of the tile, transposed: output lane (col 32db + l32)
 // gets the 8 rows 16c + {4g..4g+3, 8+4g..8+4g+3}.
@@ -104,7 +112,7 @@ template <int D>
 __device__ __forceinline__ bf16x8 lds_tr_frag(const char* lds, int tile_byte,
                                               const TileAddr<D>& a, int c, int db) {
   using C = BwdCfg<D>;
-  const char* p = lds + tile_byte + a.tr_addr[db] + c * 16 * C::ROWB;
+  const char* p = lds + tile_byte + a.tr(db) + c * 16 * C::ROWB;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(p));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -133,8 +141,11 @@ __device__ __forceinline__ void bwd_load_tile(u32x4 desc, int row0, int head_row
   }
 }
 
-template <int D, bool CAUSAL, bool FULL_D>
-__global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dkv_kernel(
+// KB key blocks of 32 per wave (KB * 128 keys per workgroup).  With KB = 2
+// every Q and dO fragment read from LDS feeds two MFMAs (half the LDS traffic
+// per MFMA); the 2 x 128 dK/dV accumulators then need one wave per SIMD.
+template <int D, bool CAUSAL, bool FULL_D, int KB>
+__global__ __launch_bounds__(kBwdThreads, KB == 1 ? 2 : 1) void attn_bwd_dkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ ws, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
@@ -155,29 +166,34 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dkv_kernel(
   const int g = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = H_Q / H_KV;
-  // Key block kb = M - 1 - m: the remap's row block m counts from the block
-  // with the least work under a causal mask, and for keys that is the last
-  // block (it is seen by the fewest query rows).
+  // Key block M - 1 - m: the remap's row block m counts from the block with
+  // the least work under a causal mask, and for keys that is the last block
+  // (it is seen by the fewest query rows).
   const WgCoord wc = wg_map(mapping, blockIdx.x, B, H_KV, M, num_xcd, 1);
-  const int key0 = (M - 1 - (int)wc.m) * kBwdBlock;
-  const int my_key = key0 + wave * 32 + l32;
+  const int key0 = (M - 1 - (int)wc.m) * kBwdBlock * KB;
+  int my_key[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) my_key[kb] = key0 + (wave * KB + kb) * 32 + l32;
   const int dd = FULL_D ? D : d;
   const uint32_t head_elems = (uint32_t)N * (uint32_t)dd;
   const uint64_t kv_head = ((uint64_t)wc.b * H_KV + wc.h) * head_elems;
   const uint64_t rows = (uint64_t)B * H_Q * N;
   const TileAddr<D> ta(lane);
 
-  // K and V of this lane's key, B operands (K^T, V^T): dims 16kc + 8g .. +7.
+  // K and V of this lane's keys, B operands (K^T, V^T): dims 16kc + 8g .. +7.
   const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + kv_head, head_elems * 2);
   const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v + kv_head, head_elems * 2);
-  bf16x8 kf[C::KC], vf[C::KC];
+  bf16x8 kf[KB][C::KC], vf[KB][C::KC];
 #pragma unroll
-  for (int kc = 0; kc < C::KC; ++kc) {
-    const int col = kc * 16 + g * 8;
-    const uint32_t off = (FULL_D || col < dd) ? (uint32_t)(my_key * dd + col) * 2u : kOutOfRange;
-    kf[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(k_rs, off, 0, 0));
-    vf[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(v_rs, off, 0, 0));
-  }
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc) {
+      const int col = kc * 16 + g * 8;
+      const uint32_t off =
+          (FULL_D || col < dd) ? (uint32_t)(my_key[kb] * dd + col) * 2u : kOutOfRange;
+      kf[kb][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(k_rs, off, 0, 0));
+      vf[kb][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(v_rs, off, 0, 0));
+    }
 
   // Padded head-dim columns are never written by the tile loads.
   if (!FULL_D) {
@@ -216,12 +232,14 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dkv_kernel(
     }
   };
 
-  f32x16 dk_acc[C::DB], dv_acc[C::DB];
+  f32x16 dk_acc[KB][C::DB], dv_acc[KB][C::DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
-    dk_acc[db] = f32x16{};
-    dv_acc[db] = f32x16{};
-  }
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      dk_acc[kb][db] = f32x16{};
+      dv_acc[kb][db] = f32x16{};
+    }
   if (n_iter > 0) {
     issue(0, 0);
     if (wave == 0) stat_load(0);
@@ -237,51 +255,84 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dkv_kernel(
       issue(it + 1, buf ^ 1);
       if (wave == 0) stat_load(it + 1);
     }
-    // S = Q K^T and dP = dO V^T for this wave's 32 keys: lane (key l32,
-    // half g) holds rows 8(r/4) + 4g + (r%4) of the tile.
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // S = Q K^T and dP = dO V^T for this wave's keys: lane (key l32 of block
+    // kb, half g) holds rows 8(r/4) + 4g + (r%4) of the tile.  Each LDS
+    // fragment feeds the KB key blocks.
+    f32x16 s[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+    }
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_frag<D>(lb, q_tile(buf), ta, kc),
-                                                  kf[kc], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_frag<D>(lb, do_tile(buf), ta, kc),
-                                                   vf[kc], dp, 0, 0, 0);
+      const bf16x8 qa = lds_row_frag<D>(lb, q_tile(buf), ta, kc);
+      const bf16x8 da = lds_row_frag<D>(lb, do_tile(buf), ta, kc);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kb][kc], s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kb][kc], dp[kb], 0, 0, 0);
+      }
     }
     const float* st = stat + buf * 64;
-    uint32_t pk[8], dsk[8];
+    uint32_t pk[KB][8], dsk[KB][8];
+    // P and dS of the tile, rounded to bf16; MASKED adds the per-element test
+    // (a row past N, a key past N, causal: a key after the row).
+    auto softmax_grad = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      const f32x4 lrow = *reinterpret_cast<const f32x4*>(st + 8 * c4 + 4 * g);
-      const f32x4 drow = *reinterpret_cast<const f32x4*>(st + 32 + 8 * c4 + 4 * g);
-      float p4[4], ds4[4];
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const f32x4 lrow = *reinterpret_cast<const f32x4*>(st + 8 * c4 + 4 * g);
+        const f32x4 drow = *reinterpret_cast<const f32x4*>(st + 32 + 8 * c4 + 4 * g);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * c4 + e;
-        const int qrow = qt * kBwdTile + 8 * c4 + 4 * g + e;
-        const bool ok = qrow < N && my_key < N && (!CAUSAL || my_key <= qrow);
-        const float p =
-            ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -lrow[e])) : 0.f;
-        p4[e] = p;
-        ds4[e] = p * (dp[r] - drow[e]);
+        for (int kb = 0; kb < KB; ++kb) {
+          float p4[4], ds4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * c4 + e;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, -lrow[e]));
+            if constexpr (MASKED) {
+              const int qrow = qt * kBwdTile + 8 * c4 + 4 * g + e;
+              const bool ok = qrow < N && my_key[kb] < N && (!CAUSAL || my_key[kb] <= qrow);
+              p = ok ? p : 0.f;
+            }
+            p4[e] = p;
+            ds4[e] = p * (dp[kb][r] - drow[e]);
+          }
+          pk[kb][2 * c4] = pack_bf16x2(p4[0], p4[1]);
+          pk[kb][2 * c4 + 1] = pack_bf16x2(p4[2], p4[3]);
+          dsk[kb][2 * c4] = pack_bf16x2(ds4[0], ds4[1]);
+          dsk[kb][2 * c4 + 1] = pack_bf16x2(ds4[2], ds4[3]);
+        }
       }
-      pk[2 * c4] = pack_bf16x2(p4[0], p4[1]);
-      pk[2 * c4 + 1] = pack_bf16x2(p4[2], p4[3]);
-      dsk[2 * c4] = pack_bf16x2(ds4[0], ds4[1]);
-      dsk[2 * c4 + 1] = pack_bf16x2(ds4[2], ds4[3]);
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS, k = the tile's rows (16 per chunk c).
+    };
+    // The test is needed only where some (row, key) pair of the wave is out:
+    // the tile holding row N-1, the key block holding key N-1, and (causal)
+    // tiles whose first row is before the wave's last key.
+    const int wave_key_end = key0 + (wave + 1) * KB * 32;  // one past the wave's keys
+    const bool full = (qt + 1) * kBwdTile <= N && wave_key_end <= N &&
+                      (!CAUSAL || qt * kBwdTile >= wave_key_end - 1);
+    if (full)
+      softmax_grad(std::false_type{});
+    else
+      softmax_grad(std::true_type{});
+    // dV^T += dO^T P and dK^T += Q^T dS, k = the tile's rows (16 per chunk c);
+    // each transposed fragment feeds the KB key blocks.
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const bf16x8 pb = __builtin_bit_cast(
-          bf16x8, u32x4{pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]});
-      const bf16x8 sb = __builtin_bit_cast(
-          bf16x8, u32x4{dsk[4 * c], dsk[4 * c + 1], dsk[4 * c + 2], dsk[4 * c + 3]});
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        dv_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            lds_tr_frag<D>(lb, do_tile(buf), ta, c, db), pb, dv_acc[db], 0, 0, 0);
-        dk_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            lds_tr_frag<D>(lb, q_tile(buf), ta, c, db), sb, dk_acc[db], 0, 0, 0);
+        const bf16x8 dot = lds_tr_frag<D>(lb, do_tile(buf), ta, c, db);
+        const bf16x8 qt_ = lds_tr_frag<D>(lb, q_tile(buf), ta, c, db);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const bf16x8 pb = __builtin_bit_cast(
+              bf16x8, u32x4{pk[kb][4 * c], pk[kb][4 * c + 1], pk[kb][4 * c + 2], pk[kb][4 * c + 3]});
+          const bf16x8 sb = __builtin_bit_cast(
+              bf16x8, u32x4{dsk[kb][4 * c], dsk[kb][4 * c + 1], dsk[kb][4 * c + 2], dsk[kb][4 * c + 3]});
+          dv_acc[kb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, pb, dv_acc[kb][db], 0, 0, 0);
+          dk_acc[kb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt_, sb, dk_acc[kb][db], 0, 0, 0);
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -289,27 +340,29 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dkv_kernel(
     __syncthreads();
   }
 
-  // Accumulator r of block db is dim 32db + 8(r/4) + 4g + (r%4) of key
-  // my_key; rows past N fall outside the buffer and are dropped.
+  // Accumulator r of block db is dim 32db + 8(r/4) + 4g + (r%4) of the key;
+  // rows past N fall outside the buffer and are dropped.
   const __amdgpu_buffer_rsrc_t dk_rs = make_rsrc(dk + kv_head, head_elems * 2);
   const __amdgpu_buffer_rsrc_t dv_rs = make_rsrc(dv + kv_head, head_elems * 2);
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int col = db * 32 + rr * 8 + g * 4;
-      if (FULL_D || col < dd) {
-        const uint32_t off = (uint32_t)(my_key * dd + col) * 2u;
-        u32x2 w;
-        w.x = pack_bf16x2(dk_acc[db][rr * 4 + 0] * scale, dk_acc[db][rr * 4 + 1] * scale);
-        w.y = pack_bf16x2(dk_acc[db][rr * 4 + 2] * scale, dk_acc[db][rr * 4 + 3] * scale);
-        __builtin_amdgcn_raw_buffer_store_b64(w, dk_rs, off, 0, 0);
-        w.x = pack_bf16x2(dv_acc[db][rr * 4 + 0], dv_acc[db][rr * 4 + 1]);
-        w.y = pack_bf16x2(dv_acc[db][rr * 4 + 2], dv_acc[db][rr * 4 + 3]);
-        __builtin_amdgcn_raw_buffer_store_b64(w, dv_rs, off, 0, 0);
+    for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int col = db * 32 + rr * 8 + g * 4;
+        if (FULL_D || col < dd) {
+          const uint32_t off = (uint32_t)(my_key[kb] * dd + col) * 2u;
+          u32x2 w;
+          w.x = pack_bf16x2(dk_acc[kb][db][rr * 4 + 0] * scale, dk_acc[kb][db][rr * 4 + 1] * scale);
+          w.y = pack_bf16x2(dk_acc[kb][db][rr * 4 + 2] * scale, dk_acc[kb][db][rr * 4 + 3] * scale);
+          __builtin_amdgcn_raw_buffer_store_b64(w, dk_rs, off, 0, 0);
+          w.x = pack_bf16x2(dv_acc[kb][db][rr * 4 + 0], dv_acc[kb][db][rr * 4 + 1]);
+          w.y = pack_bf16x2(dv_acc[kb][db][rr * 4 + 2], dv_acc[kb][db][rr * 4 + 3]);
+          __builtin_amdgcn_raw_buffer_store_b64(w, dv_rs, off, 0, 0);
+        }
       }
     }
-  }
 }
 
 template <int D, bool CAUSAL, bool FULL_D>
@@ -391,19 +444,36 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(
                                                    df[kc], dp, 0, 0, 0);
     }
     uint32_t dsk[8];
+    // dS^T of the tile; MASKED adds the per-element test (a key past N, a
+    // row past N, causal: a key after the row).
+    auto softmax_grad = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      float ds2[2];
+      for (int w = 0; w < 8; ++w) {
+        float ds2[2];
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int r = 2 * w + e;
-        const int key = j * kBwdTile + (r >> 2) * 8 + g * 4 + (r & 3);
-        const bool ok = key < N && my_row < N && (!CAUSAL || key <= my_row);
-        const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -lse2)) : 0.f;
-        ds2[e] = p * (dp[r] - drow);
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * w + e;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -lse2));
+          if constexpr (MASKED) {
+            const int key = j * kBwdTile + (r >> 2) * 8 + g * 4 + (r & 3);
+            const bool ok = key < N && my_row < N && (!CAUSAL || key <= my_row);
+            p = ok ? p : 0.f;
+          }
+          ds2[e] = p * (dp[r] - drow);
+        }
+        dsk[w] = pack_bf16x2(ds2[0], ds2[1]);
       }
-      dsk[w] = pack_bf16x2(ds2[0], ds2[1]);
-    }
+    };
+    // The test is needed only for the tile holding key N-1, the wave holding
+    // row N-1, and (causal) tiles whose last key is after the wave's first row.
+    const int wave_row0 = row0 + wave * 32;
+    const bool full = (j + 1) * kBwdTile <= N && wave_row0 + 32 <= N &&
+                      (!CAUSAL || (j + 1) * kBwdTile - 1 <= wave_row0);
+    if (full)
+      softmax_grad(std::false_type{});
+    else
+      softmax_grad(std::true_type{});
     // dQ^T += K^T dS^T (k = the tile's keys, 16 per chunk c).
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
