@@ -5,8 +5,9 @@
 // row-major bf16 (both operands K-contiguous, the layout of the attention's
 // S = Q K^T), fp32 accumulation, C rounded to bf16 (nearest-even).
 //
-// One workgroup computes one 256 x 256 tile of C with 4 waves; wave w owns
-// rows 128 (w / 2) .. +128 and columns 128 (w % 2) .. +128 as 4 x 4 blocks of
+// One workgroup computes one 256 x 256 tile of C with 8 waves (two per
+// SIMD, so one wave's LDS waits hide behind the other's MFMAs); wave w owns
+// rows 64 (w / 2) .. +64 and columns 128 (w % 2) .. +128 as 2 x 4 blocks of
 // v_mfma_f32_32x32x16_bf16.  Each block is computed transposed,
 // C^T = B A^T (A operand: 32 columns of B; B operand: 32 rows of A), so a
 // lane's 16 accumulators are 4 runs of 4 consecutive columns of one C row and
@@ -31,7 +32,8 @@ namespace attn_numa {
 constexpr int kGemmTile = 256;   // rows and columns of a C tile
 constexpr int kGemmBK = 32;      // K per step
 constexpr int kGemmStages = 4;   // LDS stages (a power of 2)
-constexpr int kGemmThreads = 256;
+constexpr int kGemmThreads = 512;
+constexpr int kGemmWaves = kGemmThreads / 64;
 constexpr int kGemmRowB = kGemmBK * 2;              // bytes of one LDS row
 constexpr int kGemmSliceB = kGemmTile * kGemmRowB;  // one operand's K slice (16 KiB)
 constexpr int kGemmStageB = 2 * kGemmSliceB;        // A slice, then B slice
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void cac_gemm_kernel(
   const u32x4 a_desc = make_desc(a + (uint64_t)tc.l * M * K, a_bytes);
   const u32x4 b_desc = make_desc(b + (uint64_t)tc.l * N * K, b_bytes);
 
-  // Tile loads: instruction i of this thread fills LDS slot P = tid + 256 i of
+  // Tile loads: instruction i of this thread fills LDS slot P = tid + 512 i of
   // a slice (row P / 4, slot P % 4 holding chunk (P % 4) ^ ((row >> 1) & 3)).
   // The row offset of the tile goes in soffset (capped at the buffer size, so
   // rows past the matrix read zero); voffset is the row within the tile and
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void cac_gemm_kernel(
     for (int i = 0; i < kGemmLoads; ++i) {
       const int kk = k0 + ld_k[i];
       const uint32_t voff = kk < K ? ld_row[i] + (uint32_t)kk * 2u : kOutOfRange;
-      const uint32_t m0b = lds_base + st * kGemmStageB + (wave + 4 * i) * 1024;
+      const uint32_t m0b = lds_base + st * kGemmStageB + (wave + kGemmWaves * i) * 1024;
       load_lds(a_desc, voff, a_soff, m0b);
       load_lds(b_desc, voff, b_soff, m0b + kGemmSliceB);
     }
@@ -92,11 +94,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void cac_gemm_kernel(
   int rd[2];
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc) rd[kc] = l32 * kGemmRowB + (((2 * kc + g) ^ ((l32 >> 1) & 3)) * 16);
-  const int wm = 128 * (wave >> 1), wn = 128 * (wave & 1);
+  const int wm = 64 * (wave >> 1), wn = 128 * (wave & 1);
 
-  f32x16 acc[4][4];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
@@ -115,38 +117,40 @@ __global__ __launch_bounds__(kGemmThreads, 1) void cac_gemm_kernel(
     else
       wait_vmcnt<0>();
     __syncthreads();
-    // All 16 operand fragments of the step first (two 16-deep K chunks),
-    // then the loads of a later step, then the 32 MFMAs: the MFMAs of chunk 0
+    // All 12 operand fragments of the step first (two 16-deep K chunks),
+    // then the loads of a later step, then the 16 MFMAs: the MFMAs of chunk 0
     // wait only for its own fragments, and chunk 1's arrive meanwhile.
     const char* sa = lb + (step & (kGemmStages - 1)) * kGemmStageB;
     const char* sb = sa + kGemmSliceB;
-    bf16x8 fa[2][4], fb[2][4];
+    bf16x8 fa[2][2], fb[2][4];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
+    for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 2; ++i)
         fa[kc][i] = *reinterpret_cast<const bf16x8*>(sa + (wm + 32 * i) * kGemmRowB + rd[kc]);
-        fb[kc][i] = *reinterpret_cast<const bf16x8*>(sb + (wn + 32 * i) * kGemmRowB + rd[kc]);
-      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[kc][j] = *reinterpret_cast<const bf16x8*>(sb + (wn + 32 * j) * kGemmRowB + rd[kc]);
+    }
     // The stage written next was last read in step - 1, which every wave
     // finished before the barrier above.
     if (step + kGemmStages - 1 < n_steps) issue(step + kGemmStages - 1);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kc][j], fa[kc][i], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // the 16 LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);  // then the 32 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // the 12 LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // then the 16 MFMAs
   }
 
   // acc[i][j] register r: C row m0 + wm + 32 i + l32, column
   // n0 + wn + 32 j + 8 (r / 4) + 4 g + (r % 4).
   const __amdgpu_buffer_rsrc_t c_rs = make_rsrc(c + (uint64_t)tc.l * M * N, c_bytes);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const int row = m0 + wm + 32 * i + l32;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
