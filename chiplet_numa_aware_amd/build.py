@@ -14,8 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn_numa.so")
 SOURCES = [os.path.join(CSRC, name) for name in (
-    "attn_fwd_d128.hip", "attn_fwd_d64.hip", "attn_bwd.hip", "attn_fwd.hip", "attn_numa.hip",
-    "cac_gemm.hip")]
+    "attn_fwd_d128.hip", "attn_fwd_d64.hip", "attn_bwd.hip", "attn_decode.hip", "attn_fwd.hip",
+    "attn_numa.hip", "cac_gemm.hip")]
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
 

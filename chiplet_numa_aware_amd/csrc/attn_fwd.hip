@@ -59,7 +59,11 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
             B * H_U * M_q * num_splits, mapping, X,
             (float)(1.4426950408889634 / std::sqrt((double)d))};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = (d <= 64) ? launch_fwd_d64(a, causal, s) : launch_fwd_d128(a, causal, s);
+  hipError_t e;
+  if (N_rows <= kDecodeMaxRows)
+    e = launch_decode(a, causal, s);
+  else
+    e = (d <= 64) ? launch_fwd_d64(a, causal, s) : launch_fwd_d128(a, causal, s);
   if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
   if (num_splits > 1) {
     const uint64_t rows = (uint64_t)B * H_Q * N_q;

@@ -25,4 +25,11 @@ struct FwdArgs {
 hipError_t launch_fwd_d64(const FwdArgs& a, int causal, hipStream_t s);
 hipError_t launch_fwd_d128(const FwdArgs& a, int causal, hipStream_t s);
 
+// Units of at most this many rows (decode; only one wave of an
+// attn_fwd_kernel workgroup would have rows) run attn_decode_kernel instead:
+// one-wave workgroups of 32 rows (attn_decode.hip).  a.W and a.M_q are
+// ignored; the launcher sizes its own grid.
+constexpr int kDecodeMaxRows = 64;
+hipError_t launch_decode(const FwdArgs& a, int causal, hipStream_t s);
+
 }  // namespace attn_numa

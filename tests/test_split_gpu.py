@@ -62,6 +62,14 @@ SPLIT_CASES = [
     (2, 16, 2, 100, 700, 64, True, 2),      # units of 800 rows: heads wrap inside blocks
     (1, 8, 1, 255, 255, 128, True, 1),      # one unit of 2040 rows, N_q == N_kv
     (1, 6, 3, 90, 2500, 56, False, 5),
+    # units of at most 64 rows run the one-wave decode kernel; the rest the
+    # 256-row kernel: both sides of the boundary
+    (1, 8, 1, 8, 500, 128, True, 3),        # packed unit of 64 rows: decode kernel
+    (1, 8, 1, 9, 500, 128, True, 3),        # packed unit of 72 rows
+    (1, 2, 2, 64, 64, 128, True, 1),        # 64 rows, one split
+    (1, 2, 2, 65, 65, 64, False, 1),        # 65 rows
+    (1, 4, 2, 3, 1000, 56, True, 4),        # decode kernel with d = 56 (padded columns)
+    (2, 3, 3, 33, 2000, 96, True, 7),       # two 32-row blocks of the decode kernel
 ]
 
 
