@@ -607,6 +607,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   f32x16 sb[2][kQB];
   scores(k_buf(0), sb[0]);
   xdl_guard_v(sb[0][0], sb[0][1]);
+  // Tile 0's first loads (K of tile 4) go to K buffer 0, which every wave
+  // has just read for these scores: no wave may issue them before all have
+  // finished reading (the reads completed before the MFMAs that used them).
+  // Every later buffer is reloaded only after the barrier that ends the tile
+  // its last reads belonged to.
+  barrier();
 
   if (wave_idle) {
     // No valid rows: only this wave's share of every tile load, with one
