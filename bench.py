@@ -15,6 +15,7 @@ Head-first.  Prints ONE JSON line on stdout (progress goes to stderr).
                   dQ, dK, dV from the forward's O and lse, one JSON line
   python bench.py --pass gemm [--workload NAME]  the CAC-scheduled GEMM
                   (cac_gemm) per tile map, with torch.mm as context
+  python bench.py --pass decode [--workload NAME] split-KV decode (HBM-bound)
 """
 from __future__ import annotations
 
@@ -48,7 +49,9 @@ KERNEL_SOURCES = {
 # Kernels whose counters a profile reports, per pass.
 PASS_KERNELS = {"fwd": ["attn_fwd_kernel"],
                 "bwd": ["attn_bwd_dkv_kernel", "attn_bwd_dq_kernel"],
-                "gemm": ["cac_gemm_kernel"]}
+                "gemm": ["cac_gemm_kernel"],
+                "decode": ["attn_decode_kernel", "attn_merge_kernel"]}
+DECODE_METRIC = "decode attention (attn_fwd_split + merge) GB/s against the HBM peak"
 KERNEL_SOURCES["gemm"] = ["chiplet_numa_aware_amd/csrc/gemm_kernel.hpp",
                           "chiplet_numa_aware_amd/csrc/cac_map.hpp",
                           "chiplet_numa_aware_amd/csrc/attn_fwd_kernel.hpp",
@@ -288,7 +291,7 @@ PROFILE_PASSES = {
 def profile_commands(workload: str, out: str, which: str = "fwd"):
     """The rocprofv3 runs whose output --summarize-profile reads."""
     bench = "python3 /root/repo/bench.py"
-    modes = "0,1,2,3" if which == "gemm" else ",".join(map(str, PROFILE_MODES))
+    modes = "0,1,2,3" if which in ("gemm", "decode") else ",".join(map(str, PROFILE_MODES))
     sel = f"--workload {workload}" + ("" if which == "fwd" else f" --pass {which}")
     one = f"{bench} {sel} --steps 1 --warmup 0 --modes {modes} --no-cpu-baseline"
     cmds = {"trace": (f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/trace -o trace -- "
@@ -755,6 +758,158 @@ def summarize_gemm_profile(directory: str, workload: str):
     print(json.dumps({k: v for k, v in data.items() if k != "commands"}, indent=1))
 
 
+def decode_describe(name) -> str:
+    B, H_Q, H_KV, N_q, N_kv, d, causal, S = SPLIT_WORKLOADS[name]
+    return (f"decode B={B} H_Q={H_Q} H_KV={H_KV} N_q={N_q} N_kv={N_kv} d={d} "
+            f"{'causal' if causal else 'non-causal'}, {S} splits")
+
+
+def run_decode(args, attn, inputs):
+    """--pass decode: attn_fwd_split (split-KV + merge) per mapping on a
+    decode workload; HBM-bound, so GB/s against the HBM peak.  One JSON line."""
+    import torch
+    B, H_Q, H_KV, N_q, N_kv, d, causal, S = SPLIT_WORKLOADS[args.workload]
+    modes = [int(m) for m in args.modes.split(",") if m.strip() != ""]
+    nbytes = split_bytes(B, H_Q, H_KV, N_q, N_kv, d, S)
+    log(f"workload {decode_describe(args.workload)}: {nbytes / 1e9:.2f} GB per call")
+    q = inputs.normal_bf16((B, H_Q, N_q, d), 1000, "cuda")
+    k = inputs.normal_bf16((B, H_KV, N_kv, d), 1001, "cuda")
+    v = inputs.normal_bf16((B, H_KV, N_kv, d), 1002, "cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H_Q, N_q), dtype=torch.float32, device="cuda")
+    o_ws = torch.empty((S, B, H_Q, N_q, d), dtype=torch.float32, device="cuda")
+    lse_ws = torch.empty((S, B, H_Q, N_q), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    results = {}
+    for mode in modes:
+        def call(stream, mode=mode):
+            attn.attn_fwd_split(q, k, v, causal=causal, num_splits=S, mapping=mode, o=o, lse=lse,
+                                o_ws=o_ws, lse_ws=lse_ws, stream=stream)
+        r = time_calls(call, max(args.steps, 10), args.warmup, 1.0)
+        r["gbs"] = nbytes / (r["kernel_ms_avg"] / 1e3) / 1e9
+        results[mode] = r
+        log(f"  {MODE_NAMES[mode]:22s} {r['gbs']:8.0f} GB/s ({100 * r['gbs'] / HBM_PEAK_GBS:.1f}% of "
+            f"the HBM peak, {r['kernel_ms_avg']:.3f} ms)")
+    headline = 3 if 3 in modes else modes[-1]
+    counters = stored_counters(args.workload, kernel_hash("decode"), "decode")
+    head = results[headline]
+    modes_out = {}
+    for mode, r in results.items():
+        entry = {"gbs": round(r["gbs"], 1), "kernel_ms_avg": round(r["kernel_ms_avg"], 4),
+                 "ms_per_step": round(r["ms_per_step"], 4)}
+        if counters and MODE_NAMES[mode] in counters["modes"]:
+            entry["l2_hit_pct"] = counters["modes"][MODE_NAMES[mode]]["l2_hit_pct"]
+        modes_out[MODE_NAMES[mode]] = entry
+    traffic = None
+    if counters and MODE_NAMES[headline] in counters["modes"]:
+        cm = counters["modes"][MODE_NAMES[headline]]
+        traffic = cm["fetch_bytes"] + cm["write_bytes"]
+    out = {
+        "metric": DECODE_METRIC,
+        "value": round(head["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": max(args.steps, 10), "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: bf16 N(0,1) Q/K/V from fixed seeds",
+        "config": {"workload": decode_describe(args.workload), "B": B, "H_Q": H_Q, "H_KV": H_KV,
+                   "N_q": N_q, "N_kv": N_kv, "d": d, "causal": causal, "splits": S,
+                   "mapping": MODE_NAMES[headline], "parallelism": "single GPU"},
+        "modes": modes_out,
+        "roofline": {"bound": "hbm", "achieved": round(head["gbs"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(head["gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "scope": "one attn_fwd_split call (decode kernel + merge kernel, one stream)"},
+        "algorithmic_bytes": nbytes,
+        "kernel_hash": kernel_hash("decode"),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def summarize_decode_profile(directory: str, workload: str):
+    """rocprofv3 CSVs of profile_commands(..., "decode") into
+    profiles/attn_decode_<workload>.md and counters_decode_<workload>.json:
+    per mapping, the decode and merge kernels' L2 hit, HBM bytes, durations."""
+    import csv
+    import glob
+    B, H_Q, H_KV, N_q, N_kv, d, causal, S = SPLIT_WORKLOADS[workload]
+    nbytes = split_bytes(B, H_Q, H_KV, N_q, N_kv, d, S)
+
+    def one(pass_name, kernel):
+        files = glob.glob(os.path.join(directory, pass_name, "*_counter_collection.csv"))
+        if not files:
+            raise SystemExit(f"missing {pass_name} counters under {directory}")
+        return _read_counters(files[0], kernel)
+
+    cal = {}
+    for name, ctr in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        v, _ = one("copy_" + name, "copyBuffer")
+        cal[ctr] = (1 << 30) / (v[-1][ctr] * 1024.0)
+    per = {}
+    for kern in PASS_KERNELS["decode"]:
+        l2, durs = one("l2", kern)
+        fe, _ = one("fetch", kern)
+        wr, _ = one("write", kern)
+        if not (len(l2) == len(fe) == len(wr) == 4):
+            raise SystemExit(f"expected one {kern} dispatch per mapping in every pass")
+        per[kern] = (l2, durs, fe, wr)
+    modes = {}
+    for m in range(4):
+        hit = sum(per[k][0][m]["TCC_HIT_sum"] for k in per)
+        miss = sum(per[k][0][m]["TCC_MISS_sum"] for k in per)
+        fetch_b = sum(per[k][2][m]["FETCH_SIZE"] for k in per) * 1024.0 * cal["FETCH_SIZE"]
+        write_b = sum(per[k][3][m]["WRITE_SIZE"] for k in per) * 1024.0 * cal["WRITE_SIZE"]
+        ms = sum(per[k][1][m] for k in per) * 1e3
+        modes[MODE_NAMES[m]] = {
+            "l2_hit_pct": round(100.0 * hit / (hit + miss), 2),
+            "fetch_bytes": fetch_b, "write_bytes": write_b,
+            "hbm_over_algorithmic": round((fetch_b + write_b) / nbytes, 3),
+            "decode_ms": round(per["attn_decode_kernel"][1][m] * 1e3, 4),
+            "merge_ms": round(per["attn_merge_kernel"][1][m] * 1e3, 4),
+            "gbs_counter_run": round(nbytes / (ms / 1e3) / 1e9, 1),
+        }
+    data = {"kernels": ["attn_numa::attn_decode_kernel", "attn_numa::attn_merge_kernel"],
+            "kernel_hash": kernel_hash("decode"), "workload": workload,
+            "description": decode_describe(workload), "algorithmic_bytes": nbytes,
+            "calibration": {"copy_bytes": 1 << 30, "scale": cal}, "modes": modes,
+            "commands": _recorded_commands(directory, workload, "decode")}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"counters_decode_{workload}.json"), "w") as f:
+        json.dump(data, f, indent=1)
+    trace = glob.glob(os.path.join(directory, "trace", "*_kernel_stats.csv"))
+    stats = []
+    if trace:
+        with open(trace[0]) as f:
+            stats = [r for r in csv.DictReader(f) if "attn_" in r["Name"]]
+    lines = [f"# attn_decode_kernel + attn_merge_kernel, {decode_describe(workload)}", "",
+             f"Kernel source hash {data['kernel_hash']} (sha256 of the decode path's sources, first 16 hex).",
+             f"Algorithmic bytes {nbytes / 1e9:.2f} GB per call (Q, K, V, O, lse and the fp32 partials "
+             "written and read back).", "", "## rocprofv3 --kernel-trace --stats", "",
+             "| kernel | calls | average ms | min ms | max ms |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {r['Name'].split('(')[0]} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+                     f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} |")
+    lines += ["", "(the trace mixes the 4 mappings, 3 calls each)", "",
+              "## Counters per mapping (decode + merge kernels, one call each)", "",
+              "| mapping | L2 hit % | HBM read GB | HBM write GB | HBM / algorithmic | decode ms | merge ms | GB/s |",
+              "|---|---|---|---|---|---|---|---|"]
+    for name, mm in modes.items():
+        lines.append(f"| {name} | {mm['l2_hit_pct']} | {mm['fetch_bytes'] / 1e9:.2f} | "
+                     f"{mm['write_bytes'] / 1e9:.3f} | {mm['hbm_over_algorithmic']} | {mm['decode_ms']} | "
+                     f"{mm['merge_ms']} | {mm['gbs_counter_run']} |")
+    lines += ["", f"HBM bytes: FETCH_SIZE and WRITE_SIZE scaled by a plain 1 GiB copy's counts "
+              f"(read x{cal['FETCH_SIZE']:.3f}, write x{cal['WRITE_SIZE']:.3f}).", "", "## Commands", "",
+              "Each pass is its own process, run as `cd /tmp && export TMPDIR=/tmp && <command>` "
+              "with the repository at /root/repo; then "
+              f"`python3 bench.py --workload {workload} --pass decode --summarize-profile DIR` wrote this file.", ""]
+    for name, cmd in data["commands"].items():
+        lines.append(f"- {name}: `{cmd}`")
+    with open(os.path.join(PROFILES, f"attn_decode_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({k: v for k, v in data.items() if k != "commands"}, indent=1))
+
+
 def run_sweep(out_path: str):
     """Times every SWEEP configuration under the four mapping modes (2 warmup
     calls, then the median of 5 calls, 10 when N <= 32K) and writes a table."""
@@ -870,14 +1025,16 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=None,
-                    choices=sorted(WORKLOADS) + sorted(GEMM_WORKLOADS),
-                    help="default: mha_128k (gemm_tall_64k_2k_8k for --pass gemm)")
+                    choices=sorted(WORKLOADS) + sorted(GEMM_WORKLOADS) + sorted(SPLIT_WORKLOADS),
+                    help="default: mha_128k (gemm_tall_64k_2k_8k for --pass gemm, "
+                         "decode_gqa64x8_b16_128k for --pass decode)")
     ap.add_argument("--modes", default="0,1,2,3",
                     help="mapping modes to time; the last one listed that is "
                          "3 (or the last one) is the headline")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "gemm"), default="fwd",
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "gemm", "decode"), default="fwd",
                     help="fwd: attn_fwd (default); bwd: attn_bwd on the forward's O, lse; "
-                         "gemm: cac_gemm (workloads gemm_*)")
+                         "gemm: cac_gemm (workloads gemm_*); decode: attn_fwd_split "
+                         "(workloads decode_*)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--sweep", metavar="OUT_MD",
@@ -892,11 +1049,16 @@ def main():
                     help="print the rocprofv3 commands for --workload, output under OUT")
     args = ap.parse_args()
     if args.workload is None:
-        args.workload = "gemm_tall_64k_2k_8k" if args.which == "gemm" else "mha_128k"
+        args.workload = {"gemm": "gemm_tall_64k_2k_8k",
+                         "decode": "decode_gqa64x8_b16_128k"}.get(args.which, "mha_128k")
     if (args.which == "gemm") != (args.workload in GEMM_WORKLOADS):
         ap.error("--pass gemm takes a gemm_* workload; the attention passes take the others")
+    if (args.which == "decode") != (args.workload in SPLIT_WORKLOADS):
+        ap.error("--pass decode takes a decode_* workload; the other passes take the others")
     if args.summarize_profile:
-        if args.which == "gemm":
+        if args.which == "decode":
+            summarize_decode_profile(args.summarize_profile, args.workload)
+        elif args.which == "gemm":
             summarize_gemm_profile(args.summarize_profile, args.workload)
         elif args.which == "bwd":
             summarize_bwd_profile(args.summarize_profile, args.workload)
@@ -940,6 +1102,9 @@ def main():
         return
     if args.which == "gemm":
         run_gemm(args, attn, inputs)
+        return
+    if args.which == "decode":
+        run_decode(args, attn, inputs)
         return
     B, H_Q, H_KV, N, d, causal = WORKLOADS[args.workload]
     modes = [int(m) for m in args.modes.split(",") if m.strip() != ""]

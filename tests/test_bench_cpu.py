@@ -35,7 +35,8 @@ TCC_COST = {"FETCH_SIZE": 3, "WRITE_SIZE": 2}
 
 
 @pytest.mark.parametrize("which,workload", [("fwd", "mha_128k"), ("bwd", "mha_32k_causal"),
-                                            ("gemm", "gemm_tall_64k_2k_8k")])
+                                            ("gemm", "gemm_tall_64k_2k_8k"),
+                                            ("decode", "decode_gqa64x8_b16_128k")])
 def test_profile_commands_respect_counter_limits(which, workload):
     cmds = bench.profile_commands(workload, "/tmp/out", which)
     assert "trace" in cmds and "--kernel-trace" in cmds["trace"] and "--pmc" not in cmds["trace"]
