@@ -482,19 +482,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // ---- running state, per query block
   f32x16 oacc[kQB][C::DB];
   float m_run[kQB], l_run[kQB];  // running max (log2 units, lazy), row-sum share
+  // Raw score above which a tile raises m: (m + slack) / scale, so that a
+  // tile's raw in-lane max is compared without scaling it.
+  float m_thr[kQB];
+  const float inv_scale_log2 = 1.f / scale_log2;
   static_for<kQB>([&](auto qbi) {
     constexpr int qb = decltype(qbi)::value;
     static_for<C::DB>([&](auto dbi) { oacc[qb][decltype(dbi)::value] = f32x16{}; });
     m_run[qb] = -INFINITY;
+    m_thr[qb] = -INFINITY;
     l_run[qb] = 0.f;
   });
 
-  // Scaled row max of a tile of scores (log2 units), both lane halves.
+  // Raw (unscaled) max of a lane's 16 scores of a tile; the two lane halves
+  // of a row are combined only when m is raised.
   auto tile_max = [&](const f32x16& s) {
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    return xhalf_max(mx) * scale_log2;
+    return mx;
   };
   // The running max m is raised only when a tile's max exceeds it by more
   // than the slack (always on a row's first tile, where m = -inf); the
@@ -503,11 +509,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // loop makes the compiler copy O out of the MFMA accumulators and back on
   // every tile.  Every s_barrier stays matched: the raise path has none.
   auto needs_raise = [&](int qb, float mx) {
-    return __builtin_amdgcn_ballot_w64(mx > m_run[qb] + kRescaleSlack) != 0;
+    return __builtin_amdgcn_ballot_w64(mx > m_thr[qb]) != 0;
   };
   auto raise_max = [&](int qb, float mx) {
     if (!needs_raise(qb, mx)) return;
-    const float m_new = fmaxf(m_run[qb], mx);
+    // Both lane halves of a row take the same m (they hold the same rows).
+    const float m_new = fmaxf(m_run[qb], xhalf_max(mx) * scale_log2);
     // A lane with no visible key yet keeps alpha = 1 (no -inf - -inf).
     const float alpha = (m_new == -INFINITY)
                             ? 1.f
@@ -519,6 +526,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     static_for<C::DB>([&](auto dbi) { xdl_guard_a(oacc[qb][decltype(dbi)::value]); });
     l_run[qb] *= alpha;
     m_run[qb] = m_new;
+    m_thr[qb] = (m_new + kRescaleSlack) * inv_scale_log2;
   };
   // Offset subtracted before exponentiating (0 while a row has seen no key).
   auto m_offset = [&](int qb) { return (m_run[qb] == -INFINITY) ? 0.f : m_run[qb]; };
@@ -616,12 +624,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 
   if (wave_idle) {
     // No valid rows: only this wave's share of every tile load, with one
-    // barrier per tile like the computing waves, and the same two tiles of
-    // loads in flight at each barrier (tiles past the end read nothing).
+    // barrier per tile like the computing waves, and the same loads in
+    // flight at each barrier (tiles past the end read nothing).
     for (int jj = 0; jj < n_tiles; ++jj) {
       load_k(jj + kStages);
       load_v(jj + kStages - 1);
-      wait_vmcnt<2 * 2 * C::LOADS>();
+      wait_vmcnt<3 * C::LOADS>();
       barrier();
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -634,6 +642,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   static_assert(TS::valid(), "tile schedule breaks a data dependency");
   static_assert(kStages == 4, "the steady loop is unrolled over four phases");
   constexpr int kDist = 3;  // LDS fragment prefetch distance (fragments)
+  static_assert(kDist <= C::KC, "a ring head holds K fragments only");
   float mx_cur[kQB];
   static_for<kQB>([&](auto qbi) {
     constexpr int qb = decltype(qbi)::value;
@@ -641,6 +650,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   });
   // Byte offsets of the next K and V tiles to load (tiles j+4 and j+3).
   uint32_t k_soff = tile_soff(kStages), v_soff = tile_soff(kStages - 1);
+  // The first kDist K fragments a steady tile j needs (K of tile j+1) are
+  // read before the barrier that opens it, at the end of tile j-1, so that
+  // its first MFMAs do not wait for LDS reads issued after that barrier.
+  // That needs K of tile j+1 to have landed one barrier earlier than the
+  // V data: each barrier that ends a tile t waits for the K loads issued in
+  // tile t-1 (loads go out K before V, so vmcnt leaves only V of tile t-1 and
+  // tile t's loads in flight).
+  bf16x8 ring_head[kDist];
+  static_for<kDist>([&](auto fi) {
+    constexpr int f = decltype(fi)::value;
+    ring_head[f] = k_frag(k_buf(1), f);
+  });
 
   // One steady tile in buffer phase P = j % 4.  Returns false, having done
   // nothing, at the end of the steady tiles or when the running max must be
@@ -668,7 +689,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     bf16x8 ring[kDist + 1];
     static_for<kDist>([&](auto fi) {
       constexpr int f = decltype(fi)::value;
-      ring[f] = frag(f);
+      ring[f] = ring_head[f];
     });
     f32x16* const s_cur = sb[cur];
     f32x16* const sn = sb[nxt];
@@ -739,14 +760,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       });
       __builtin_amdgcn_sched_barrier(0);
     });
+    // Head of the next tile's ring: K of tile j+2, whose loads (issued in
+    // tile j-2) the barrier that ended tile j-1 covers.
+    constexpr int kb_next = ((P + 2) % kStages) * C::TILE_B;
+    static_for<kDist>([&](auto fi) {
+      constexpr int f = decltype(fi)::value;
+      ring_head[f] = k_frag(kb_next, f);
+    });
     static_for<kQB>([&](auto qbi) {
       constexpr int qb = decltype(qbi)::value;
-      mx_cur[qb] = xhalf_max(mx[qb]) * scale_log2;
+      mx_cur[qb] = mx[qb];
     });
     k_soff = min(k_soff + tile_bytes, (uint32_t)head_bytes);
     v_soff = min(v_soff + tile_bytes, (uint32_t)head_bytes);
-    // K of tile j+2 and V of tile j+1 were loaded during tile j-2.
-    wait_vmcnt<2 * 2 * C::LOADS>();
+    // After this barrier: V of tile j+1 (loaded during tile j-2) and K of
+    // tile j+3 (loaded during tile j-1) have landed.
+    wait_vmcnt<3 * C::LOADS>();
     barrier();
     ++j;
     return true;
