@@ -641,7 +641,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // this tile's and the previous tile's loads stay in flight.
   static_assert(TS::valid(), "tile schedule breaks a data dependency");
   static_assert(kStages == 4, "the steady loop is unrolled over four phases");
-  constexpr int kDist = 3;  // LDS fragment prefetch distance (fragments)
+  constexpr int kDist = 4;  // LDS fragment prefetch distance (fragments)
   static_assert(kDist <= C::KC, "a ring head holds K fragments only");
   float mx_cur[kQB];
   static_for<kQB>([&](auto qbi) {
@@ -731,20 +731,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     static_for<TS::T>([&](auto ti) {
       constexpr int t = decltype(ti)::value;
       constexpr int f = t / kQB;  // fragment of this bundle's MFMA
-      // LDS-direct loads in the first bundles: pairs when d == D.
-      if constexpr (kPairs) {
-        constexpr int NPAIR = C::LOADS / 2;
-        if constexpr (t < NPAIR)
-          load_lds_pair<kdst + t * 4096>(k_desc, ld_off[2 * t], k_soff, m0_wave);
-        else if constexpr (t < 2 * NPAIR)
-          load_lds_pair<vdst + (t - NPAIR) * 4096>(v_desc, ld_off[2 * (t - NPAIR)], v_soff,
-                                                   m0_wave);
-      } else {
-        if constexpr (t < C::LOADS)
-          load_lds(k_desc, ld_off[t], k_soff, m0_wave + kdst + t * 2048);
-        else if constexpr (t < 2 * C::LOADS)
-          load_lds(v_desc, ld_off[t - C::LOADS], v_soff, m0_wave + vdst + (t - C::LOADS) * 2048);
-      }
       if constexpr (t % kQB == 0 && f + kDist < TS::FRAGS)
         ring[(f + kDist) % (kDist + 1)] = frag(f + kDist);
       const bf16x8 a = ring[f % (kDist + 1)];
@@ -761,6 +747,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
         mfma_out<(pack_b >= t - 2) ? 3 : 0>(
             oacc[qb][db], a,
             __builtin_bit_cast(bf16x8, u32x4{pk[ch][0], pk[ch][1], pk[ch][2], pk[ch][3]}));
+      }
+      // LDS-direct loads in the first bundles, after the MFMA (the first
+      // MFMA of a tile then issues right after the barrier): pairs when
+      // d == D.
+      if constexpr (kPairs) {
+        constexpr int NPAIR = C::LOADS / 2;
+        if constexpr (t < NPAIR)
+          load_lds_pair<kdst + t * 4096>(k_desc, ld_off[2 * t], k_soff, m0_wave);
+        else if constexpr (t < 2 * NPAIR)
+          load_lds_pair<vdst + (t - NPAIR) * 4096>(v_desc, ld_off[2 * (t - NPAIR)], v_soff,
+                                                   m0_wave);
+      } else {
+        if constexpr (t < C::LOADS)
+          load_lds(k_desc, ld_off[t], k_soff, m0_wave + kdst + t * 2048);
+        else if constexpr (t < 2 * C::LOADS)
+          load_lds(v_desc, ld_off[t - C::LOADS], v_soff, m0_wave + vdst + (t - C::LOADS) * 2048);
       }
       // With D = 64 (about 9 VALU issue slots per MFMA) the bundle's VALU
       // slice is kept after its MFMA: left free, the compiler moves some
