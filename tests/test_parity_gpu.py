@@ -188,3 +188,28 @@ def test_repeated_launches_identical(shape):
             first = (o.clone(), lse.clone())
         else:
             assert torch.equal(o, first[0]) and torch.equal(lse, first[1]), f"launch {i} differs"
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_running_max_raised_inside_steady_tiles(d):
+    """Key rows scaled by 1 + j/64, so the scores of later key tiles grow and
+    the running max is raised every few tiles in the middle of the pipelined
+    loop (a raise leaves the loop and resumes at the same tile); every
+    element against the oracle, the same result under all 8 mappings, and
+    repeated launches bit-identical."""
+    B, H, N = 1, 2, 2048
+    say(f"case growing scores d={d}")
+    q, k, v = inputs.make_qkv(B, H, H, N, d, seed=123 + d, device="cpu")
+    grow = (1.0 + torch.arange(N, dtype=torch.float32) / 64.0).view(1, 1, N, 1)
+    k = (k.float() * grow).to(torch.bfloat16)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    for causal in (False, True):
+        o_ref, lse_ref = _oracle(q, k, v, causal)
+        o0, l0 = _run(q, k, v, causal, 0)
+        assert_close(f64(o0), f64(l0), o_ref, lse_ref, f"growing d={d} causal={causal}")
+        for mapping in range(1, 8):
+            o, lse = _run(q, k, v, causal, mapping)
+            assert torch.equal(o, o0) and torch.equal(lse, l0), f"mapping {mapping} differs"
+        for _ in range(3):
+            o, lse = _run(q, k, v, causal, 3)
+            assert torch.equal(o, o0) and torch.equal(lse, l0), "repeated launch differs"
