@@ -298,8 +298,17 @@ struct TileSchedule {
   }
 };
 
+// Waves per SIMD: D = 128 needs ~484 registers per wave (O and Q of two
+// query blocks in AGPRs), so one.  D = 64 fits in 256 (a few values spill
+// outside the steady loop), and two waves per SIMD (two workgroups per CU)
+// let one wave's softmax VALU work issue beside the other's MFMAs: the D = 64
+// tile has about nine VALU issue slots per MFMA, more than one wave hides
+// under its own MFMAs (measured 13-16% faster than one wave per SIMD).
+template <int D>
+constexpr int kWavesPerSimd = D == 64 ? 2 : 1;
+
 template <int D, bool CAUSAL, bool FULL_D>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, int B, int H_U, int H_KV, int N_rows, int pos_mod,

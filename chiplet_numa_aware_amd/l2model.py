@@ -33,13 +33,23 @@ import numpy as np
 
 BLOCK_N = 32           # keys per K/V tile of the kernel
 L2_BYTES = 4 << 20     # per XCD on MI355X
-SLOTS_PER_XCD = 32     # 32 CUs per XCD x one workgroup per CU
+CUS_PER_XCD = 32
+
+
+def workgroups_per_cu(d: int) -> int:
+    """Forward workgroups resident per CU: one with head dim > 64 (one
+    256-thread workgroup fills the CU's registers), two with head dim <= 64
+    (padded to 64, two waves per SIMD)."""
+    return 2 if d <= 64 else 1
 
 
 def predict_hit(B: int, H_Q: int, H_KV: int, N: int, d: int, causal: bool,
-                mapping: int, num_xcd: int = 8, slots: int = SLOTS_PER_XCD,
+                mapping: int, num_xcd: int = 8, slots: int | None = None,
                 l2_bytes: int = L2_BYTES) -> float:
-    """Predicted fraction of K/V tile reads that hit in L2."""
+    """Predicted fraction of K/V tile reads that hit in L2.  ``slots``:
+    workgroups an XCD runs at once (default: its CUs x workgroups_per_cu)."""
+    if slots is None:
+        slots = CUS_PER_XCD * workgroups_per_cu(d)
     from . import attn_block_m, attn_wg_map  # the library's host table
     G = H_Q // H_KV
     block_m = attn_block_m()
