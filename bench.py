@@ -126,6 +126,26 @@ def split_bytes(B, H_Q, H_KV, N_q, N_kv, d, S) -> float:
     return 2.0 * (2 * rows * d + 2 * B * H_KV * N_kv * d) + 4 * rows + ws
 
 
+def device_info() -> dict:
+    """GPU, partition and software versions the numbers were taken with."""
+    import torch
+
+    import chiplet_numa_aware_amd as attn
+    props = torch.cuda.get_device_properties(0)
+    xcd = attn.attn_num_xcd()
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+            "cus": props.multi_processor_count, "xcds": xcd,
+            "partition": "SPX (one device spans all 8 XCDs)" if xcd == 8 else f"{xcd} XCDs",
+            "rocm": rocm, "hip": torch.version.hip,
+            "host_cores": len(os.sched_getaffinity(0))}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -1175,6 +1195,7 @@ def main():
             "traffic": traffic,
         },
         "kernel_hash": khash,
+        "device": device_info(),
     }
     if 0 in results and headline in results and headline != 0:
         out["speedup_vs_naive_block_first"] = round(
