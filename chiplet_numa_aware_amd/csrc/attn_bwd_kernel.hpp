@@ -24,7 +24,8 @@
 // P or dS, rounded to bf16, feed the next MFMA from registers as the B operand
 // with the k order the transposing LDS reads (ds_read_b64_tr_b16) produce for
 // the A operand.  LDS tiles are 32 rows of D/8 16-byte chunks, chunk c of row
-// r at slot c ^ (r & 7) (conflict-free for both read kinds).
+// r at slot c ^ (r & 7), the forward kernel's layout (chosen for 32 LDS banks;
+// gfx950 has 64, where its reads are 2- to 4-way bank-conflicted).
 #pragma once
 
 #include <hip/hip_runtime.h>

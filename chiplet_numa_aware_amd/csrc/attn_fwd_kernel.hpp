@@ -29,8 +29,10 @@
 //     loads with the LDS-direct bit, no staging registers), four buffers per
 //     operand, so a tile's load has two key tiles of compute to land.  A tile
 //     is 32 rows of D/8 16-byte chunks; chunk c of row r sits at slot
-//     c ^ (r & 7), which keeps both the K operand reads and the transposing V
-//     reads free of bank conflicts.
+//     c ^ (r & 7).  In gfx950's 64-bank LDS that leaves the K operand reads
+//     2-way and the transposing V reads 4-way bank-conflicted at D = 128; the
+//     operand ring reads four fragments ahead, which hides the extra cycles
+//     (a conflict-free swizzle measured no faster).
 //   * software pipeline, one barrier per key tile j: the score MFMAs of tile
 //     j+1 are issued with the softmax and P V of tile j; a steady tile is a
 //     static sequence of MFMA "bundles" (see TileSchedule).  The steady loop
