@@ -24,8 +24,7 @@
 // P or dS, rounded to bf16, feed the next MFMA from registers as the B operand
 // with the k order the transposing LDS reads (ds_read_b64_tr_b16) produce for
 // the A operand.  LDS tiles are 32 rows of D/8 16-byte chunks, chunk c of row
-// r at slot c ^ (r & 7), the forward kernel's layout (chosen for 32 LDS banks;
-// gfx950 has 64, where its reads are 2- to 4-way bank-conflicted).
+// r at slot c ^ swz(r) (BwdCfg).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -75,31 +74,56 @@ struct BwdCfg {
   static constexpr int TILE_B = kBwdTile * ROWB;
   static constexpr int SLOTS = kBwdTile * CPR / kBwdThreads;  // 16-byte loads per thread
   static_assert(SLOTS * kBwdThreads == kBwdTile * CPR, "a tile splits into the workgroup");
+  // Chunk swizzle.  gfx950's LDS has 64 banks of 4 bytes and serves 16 lanes
+  // of a 16-byte read (here: 16 consecutive rows, one chunk) and 32 lanes of
+  // a transposing 8-byte read (4 consecutive rows from a multiple of 4, one
+  // aligned group of 4 chunks) per cycle.  D = 64 (128-byte rows, which
+  // alternate bank halves): swz spreads the 8 rows of one parity over the 8
+  // slots and sends rows 4i and 4i+2 to different groups of 4, so both reads
+  // are free of bank conflicts.  D = 128 keeps r & 7 (2-way conflicts on the
+  // first read kind, 4-way on the second): a conflict-free swizzle there XORs
+  // four bits of the chunk index, which doubles the per-lane address table
+  // below; the dK/dV kernel then spills, and measured 8% slower under a
+  // causal mask.
+  static __device__ __forceinline__ constexpr int swz(int r) {
+    return D == 64 ? 4 * ((r >> 1) & 1) + ((r >> 2) & 3) : (r & 7);
+  }
 };
 
 // Per-lane LDS addresses of the two operand kinds, for a tile at byte 0.
-// The swizzle XORs the low three bits of the chunk index only, so chunks
-// 8..15 of a row sit 128 bytes after chunks 0..7: only the first eight
-// chunks' addresses are kept, and the rest become instruction offsets.
+// With D = 128 the swizzle XORs the low three bits of the chunk index only,
+// and rows r and r + 8 share it, so chunks 8..15 of a row sit 128 bytes after
+// chunks 0..7 and the second half of a transposing read 8 rows further: only
+// the first eight chunks' addresses are kept, and the rest become
+// instruction offsets.  With D = 64 rows r and r + 8 differ in swizzle, so
+// both halves of a transposing read keep an address.
 template <int D>
 struct TileAddr {
   using C = BwdCfg<D>;
   static constexpr int NR = C::KC < 4 ? C::KC : 4, NT = C::DB < 2 ? C::DB : 2;
-  int row_addr[NR];  // 16-byte read of row l32, chunk 2kc + g
-  int tr_addr[NT];   // transposing read (4 rows x 8 bytes per lane group)
+  static constexpr int NH = D == 64 ? 2 : 1;
+  int row_addr[NR];     // 16-byte read of row l32, chunk 2kc + g
+  int tr_addr[NT][NH];  // transposing read (4 rows x 8 bytes per lane group), rows + 8h
   __device__ __forceinline__ TileAddr(int lane) {
     const int g = lane >> 5, l32 = lane & 31;
 #pragma unroll
     for (int kc = 0; kc < NR; ++kc)
-      row_addr[kc] = l32 * C::ROWB + (((kc * 2 + g) ^ (l32 & 7)) * 16);
+      row_addr[kc] = l32 * C::ROWB + (((kc * 2 + g) ^ C::swz(l32)) * 16);
     const int j = lane & 15, kk = j >> 2, qq = j & 3, dhalf = (lane >> 4) & 1;
     const int krow = 4 * g + kk, w = 2 * dhalf + (qq >> 1);
 #pragma unroll
     for (int db = 0; db < NT; ++db)
-      tr_addr[db] = krow * C::ROWB + (((4 * db + w) ^ krow) * 16) + (qq & 1) * 8;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        tr_addr[db][h] = (krow + 8 * h) * C::ROWB +
+                         (((4 * db + w) ^ C::swz(krow + 8 * h)) * 16) + (qq & 1) * 8;
   }
   __device__ __forceinline__ int row(int kc) const { return row_addr[kc % NR] + (kc / NR) * 128; }
-  __device__ __forceinline__ int tr(int db) const { return tr_addr[db % NT] + (db / NT) * 128; }
+  // Second half (rows + 8) of a transposing read.
+  __device__ __forceinline__ int tr(int db, int h) const {
+    if constexpr (NH == 2) return tr_addr[db % NT][h] + (db / NT) * 128;
+    else return tr_addr[db % NT][0] + (db / NT) * 128 + h * 8 * C::ROWB;
+  }
 };
 
 template <int D>
@@ -113,11 +137,11 @@ template <int D>
 __device__ __forceinline__ bf16x8 lds_tr_frag(const char* lds, int tile_byte,
                                               const TileAddr<D>& a, int c, int db) {
   using C = BwdCfg<D>;
-  const char* p = lds + tile_byte + a.tr(db) + c * 16 * C::ROWB;
+  const char* p = lds + tile_byte + c * 16 * C::ROWB;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(p));
+      (__attribute__((address_space(3))) i16x4*)(p + a.tr(db, 0)));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(p + 8 * C::ROWB));
+      (__attribute__((address_space(3))) i16x4*)(p + a.tr(db, 1)));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -135,7 +159,7 @@ __device__ __forceinline__ void bwd_load_tile(u32x4 desc, int row0, int head_row
   for (int i = 0; i < C::SLOTS; ++i) {
     const int P = tid + kBwdThreads * i;
     const int row = P / C::CPR;
-    const int chunk = (P % C::CPR) ^ (row & 7);
+    const int chunk = (P % C::CPR) ^ C::swz(row);
     const uint32_t voff = (FULL_D || chunk * 8 < dd) ? (uint32_t)(row * dd + chunk * 8) * 2u
                                                      : kOutOfRange;
     load_lds(desc, voff, soff, lds_base + tile_byte + (wave + 4 * i) * 1024);
