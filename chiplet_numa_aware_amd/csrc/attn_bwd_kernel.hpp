@@ -77,26 +77,34 @@ struct BwdCfg {
   // Chunk swizzle.  gfx950's LDS has 64 banks of 4 bytes and serves 16 lanes
   // of a 16-byte read (here: 16 consecutive rows, one chunk) and 32 lanes of
   // a transposing 8-byte read (4 consecutive rows from a multiple of 4, one
-  // aligned group of 4 chunks) per cycle.  D = 64 (128-byte rows, which
-  // alternate bank halves): swz spreads the 8 rows of one parity over the 8
-  // slots and sends rows 4i and 4i+2 to different groups of 4, so both reads
-  // are free of bank conflicts.  D = 128 keeps r & 7 (2-way conflicts on the
-  // first read kind, 4-way on the second): a conflict-free swizzle there XORs
-  // four bits of the chunk index, which doubles the per-lane address table
-  // below; the dK/dV kernel then spills, and measured 8% slower under a
-  // causal mask.
+  // aligned group of 4 chunks) per cycle; both are free of bank conflicts.
+  // D = 128 (256-byte rows, all starting at bank 0): a permutation over
+  // r mod 16 whose value / 4 differs among 4 consecutive rows.  D = 64
+  // (128-byte rows, alternating bank halves): the 8 rows of one parity go to
+  // the 8 slots, rows 4i and 4i+2 to different groups of 4.
   static __device__ __forceinline__ constexpr int swz(int r) {
-    return D == 64 ? 4 * ((r >> 1) & 1) + ((r >> 2) & 3) : (r & 7);
+    return D == 64 ? 4 * ((r >> 1) & 1) + ((r >> 2) & 3) : 4 * (r & 3) + ((r >> 2) & 3);
   }
 };
 
+// a ^ K where it is used: the volatile asm keeps the compiler from hoisting
+// the XORed addresses out of the loops into registers of their own.
+// (k is a constant once the loops around the reads are unrolled.)
+__device__ __forceinline__ int xor_at_use(int a, int k) {
+  if (k == 0) return a;
+  int r;
+  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(k), "v"(a));
+  return r;
+}
+
 // Per-lane LDS addresses of the two operand kinds, for a tile at byte 0.
-// With D = 128 the swizzle XORs the low three bits of the chunk index only,
-// and rows r and r + 8 share it, so chunks 8..15 of a row sit 128 bytes after
-// chunks 0..7 and the second half of a transposing read 8 rows further: only
-// the first eight chunks' addresses are kept, and the rest become
-// instruction offsets.  With D = 64 rows r and r + 8 differ in swizzle, so
-// both halves of a transposing read keep an address.
+// D = 128: only the addresses of chunks 0..7 are kept.  Chunk c + 8 sits at
+// slot (c ^ swz) ^ 8, i.e. the address XOR 128; row r + 8 (the second half of
+// a transposing read) has swz(r) ^ 2, i.e. the address XOR 32, 8 rows
+// further.  The XORs take one VALU op per read instead of twice the address
+// registers (which made the dK/dV kernel spill).  D = 64: rows r and r + 8
+// differ in the group bit of the swizzle, so both halves of a transposing
+// read keep an address.
 template <int D>
 struct TileAddr {
   using C = BwdCfg<D>;
@@ -118,11 +126,15 @@ struct TileAddr {
         tr_addr[db][h] = (krow + 8 * h) * C::ROWB +
                          (((4 * db + w) ^ C::swz(krow + 8 * h)) * 16) + (qq & 1) * 8;
   }
-  __device__ __forceinline__ int row(int kc) const { return row_addr[kc % NR] + (kc / NR) * 128; }
-  // Second half (rows + 8) of a transposing read.
+  __device__ __forceinline__ int row(int kc) const {
+    return xor_at_use(row_addr[kc % NR], (kc / NR) * 128);
+  }
+  // h = 1: the second half (rows + 8) of a transposing read.
   __device__ __forceinline__ int tr(int db, int h) const {
-    if constexpr (NH == 2) return tr_addr[db % NT][h] + (db / NT) * 128;
-    else return tr_addr[db % NT][0] + (db / NT) * 128 + h * 8 * C::ROWB;
+    if constexpr (NH == 2)
+      return xor_at_use(tr_addr[db % NT][h], (db / NT) * 128);
+    else
+      return xor_at_use(tr_addr[db % NT][0], (db / NT) * 128 + h * 32) + h * 8 * C::ROWB;
   }
 };
 
