@@ -44,11 +44,15 @@ constexpr int kGemmStageB = 2 * kGemmSliceB;        // A slice, then B slice
 constexpr int kGemmLoads = kGemmSliceB / 16 / kGemmThreads;  // 16-byte loads per thread per slice
 static_assert(kGemmLoads * 16 * kGemmThreads == kGemmSliceB, "a slice splits into the workgroup");
 
-// Slot of chunk c of LDS row r is c ^ gemm_swz(r): rows of 64 bytes (4
-// chunks) pair up in a 128-byte bank line, rows of 128 bytes fill one; either
-// way 8 consecutive rows reading the same chunk hit 8 distinct 16-byte slots.
+// Slot of chunk c of LDS row r is c ^ gemm_swz(r).  gfx950's LDS has 64
+// banks of 4 bytes (a 256-byte line) and serves a 16-byte read 16 lanes per
+// cycle, here 16 consecutive rows reading one chunk.  Rows of 128 bytes (8
+// chunks) alternate between the two halves of a line, and the 8 rows of one
+// parity take 8 distinct slots; rows of 64 bytes (4 chunks) share a line four
+// at a time, and the 4 rows at one position take 4 distinct slots.  Either
+// way the 16 reads cover the 64 banks once.
 __device__ __forceinline__ int gemm_swz(int r) {
-  return kGemmCPR == 4 ? ((r >> 1) & 3) : (r & 7);
+  return kGemmCPR == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7);
 }
 
 __global__ __launch_bounds__(kGemmThreads, 1) void cac_gemm_kernel(
