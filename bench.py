@@ -180,10 +180,17 @@ def kernel_hash(which: str = "fwd") -> str:
     return h.hexdigest()[:16]
 
 
+def counters_path(workload: str, which: str = "fwd") -> str:
+    name = {"gemm": f"counters_gemm_{workload}.json",
+            "decode": f"counters_decode_{workload}.json"}.get(
+                which, f"counters_attn_{which}_{workload}.json")
+    return os.path.join(PROFILES, name)
+
+
 def stored_counters(workload: str, khash: str, which: str = "fwd"):
     """Counter-derived figures (L2 hit, HBM bytes) kept under profiles/ for
     this workload, or None when absent or taken on another kernel version."""
-    path = os.path.join(PROFILES, f"counters_attn_{which}_{workload}.json")
+    path = counters_path(workload, which)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -191,6 +198,19 @@ def stored_counters(workload: str, khash: str, which: str = "fwd"):
     if data.get("kernel_hash") != khash:
         return None
     return data
+
+
+def counters_source(workload: str, khash: str, which: str = "fwd", counters=None):
+    """Where a line's l2_hit_pct / traffic come from: a committed rocprofv3
+    counter summary of the same kernel sources (its file and hash), taken in
+    a separate profiled run, not in this timed one."""
+    if counters is None:
+        return None
+    return {"file": os.path.relpath(counters_path(workload, which), ROOT),
+            "kernel_hash": khash,
+            "note": "rocprofv3 counter passes recorded in that file (a separate "
+                    "profiled process, possibly another box); not measured in "
+                    "this timed run"}
 
 
 def time_mode(attn, q, k, v, o, lse, causal, mode, steps, warmup, flops):
@@ -614,6 +634,7 @@ def run_bwd(args, attn, inputs):
                      "traffic": traffic,
                      "scope": "one attn_bwd call (its three kernels, one stream)"},
         "kernel_hash": kernel_hash("bwd"),
+        "counters_source": counters_source(args.workload, kernel_hash("bwd"), "bwd", counters),
     }
     if 0 in results and headline != 0:
         out["speedup_vs_naive_block_first"] = round(
@@ -691,6 +712,7 @@ def run_gemm(args, attn, inputs):
                      "frac": round(head["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
         "kernel_hash": kernel_hash("gemm"),
+        "counters_source": counters_source(args.workload, kernel_hash("gemm"), "gemm", counters),
     }
     if 0 in results and headline != 0:
         out["speedup_vs_naive_row_major"] = round(results[0]["kernel_ms_avg"] / head["kernel_ms_avg"], 4)
@@ -843,6 +865,7 @@ def run_decode(args, attn, inputs):
                      "scope": "one attn_fwd_split call (decode kernel + merge kernel, one stream)"},
         "algorithmic_bytes": nbytes,
         "kernel_hash": kernel_hash("decode"),
+        "counters_source": counters_source(args.workload, kernel_hash("decode"), "decode", counters),
     }
     print(json.dumps(out), flush=True)
 
@@ -1195,6 +1218,7 @@ def main():
             "traffic": traffic,
         },
         "kernel_hash": khash,
+        "counters_source": counters_source(args.workload, khash, "fwd", counters),
         "device": device_info(),
     }
     if 0 in results and headline in results and headline != 0:

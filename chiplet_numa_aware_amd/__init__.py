@@ -5,11 +5,11 @@ passes runs in
 the library's HIP kernels.  torch provides device memory and streams.  The
 entry points have the names of the C ABI in include/attn_numa.h:
 
-* ``attn_fwd(q, k, v, causal=False, mapping=3, o=None, lse=None)``
-* ``attn_fwd_split(q, k, v, causal=False, num_splits=1, mapping=3, ...)``
+* ``attn_fwd(q, k, v, causal=False, mapping=None, o=None, lse=None)``
+* ``attn_fwd_split(q, k, v, causal=False, num_splits=1, mapping=None, ...)``
 * ``attn_split_chunk(N_kv, num_splits)``
 * ``attn_merge(o_parts, lse_parts, o=None, lse=None)``
-* ``attn_bwd(q, k, v, o, dout, lse, causal=False, mapping=3, ...)``
+* ``attn_bwd(q, k, v, o, dout, lse, causal=False, mapping=None, ...)``
 * ``cac_gemm(a, b, mapping=3, group_m=0, group_n=0, c=None)`` (include/cac_gemm.h)
 * ``cac_gemm_map(mapping, L, M, N, group_m, group_n, num_xcd)``
 * ``cac_gemm_tile()``
@@ -18,6 +18,10 @@ entry points have the names of the C ABI in include/attn_numa.h:
 * ``attn_block_m()``
 * ``attn_probe_placement(mapping, B, H_Q, H_KV, N, out=None)``
 * ``attn_strerror(code)``
+
+``mapping=None`` is swizzled head-first (3), and under a causal mask
+3 | LONGEST_FIRST | BALANCED_SPLIT (15).  Caller-given outputs and
+workspaces are checked (device, shape, dtype, contiguity) before any launch.
 
 The library must be built (``python -m chiplet_numa_aware_amd.build``);
 there is no fallback: a missing library raises.
@@ -36,6 +40,7 @@ __all__ = [
     "attn_wg_map", "attn_num_xcd", "attn_block_m",
     "attn_probe_placement", "attn_strerror", "library_path", "load_library",
     "MAPPINGS", "row_blocks", "num_workgroups", "BLOCK_M",
+    "LONGEST_FIRST", "BALANCED_SPLIT", "DEFAULT_MAPPING", "DEFAULT_CAUSAL_MAPPING",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -48,6 +53,14 @@ MAPPINGS = {
     "swizzled_block_first": 2,
     "swizzled_head_first": 3,
 }
+
+# Added to a mode (ATTN_MAP_LONGEST_FIRST, ATTN_MAP_BALANCED_SPLIT).
+LONGEST_FIRST = 4
+BALANCED_SPLIT = 8
+# Default mappings: swizzled head-first, and under a causal mask also longest
+# first and balanced splits.
+DEFAULT_MAPPING = 3
+DEFAULT_CAUSAL_MAPPING = 3 | LONGEST_FIRST | BALANCED_SPLIT
 
 # Tile map modes of cac_gemm (CAC_MAP_* in include/cac_gemm.h).
 CAC_MAPPINGS = {
@@ -139,10 +152,33 @@ def num_workgroups(B: int, H_Q: int, N: int) -> int:
     return B * H_Q * row_blocks(N)
 
 
-def _mapping_id(mapping) -> int:
+def _mapping_id(mapping, causal: bool = False) -> int:
+    """Mode id of ``mapping`` (a name or an int).  None picks the default:
+    swizzled head-first, plus longest first and balanced splits under a
+    causal mask (the order that keeps each ACC's concurrent workgroups
+    together in the K/V stream and balances the causal work of ACCs split
+    between two XCDs; for a non-causal call both bits change nothing but the
+    order of equal-length row blocks)."""
+    if mapping is None:
+        return DEFAULT_CAUSAL_MAPPING if causal else DEFAULT_MAPPING
     if isinstance(mapping, str):
         return MAPPINGS[mapping]
     return int(mapping)
+
+
+def _check_out(name: str, t, shape, dtype, device: torch.device):
+    """A caller-given output or workspace: a contiguous tensor of exactly
+    ``shape`` and ``dtype`` on the inputs' GPU.  Raised before any launch,
+    so that a wrong buffer is a ValueError and not a GPU memory fault."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device} (the inputs' device), not {t.device}")
 
 
 def _stream_handle(stream, device) -> int:
@@ -152,7 +188,7 @@ def _stream_handle(stream, device) -> int:
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-             causal: bool = False, mapping=3, o: torch.Tensor | None = None,
+             causal: bool = False, mapping=None, o: torch.Tensor | None = None,
              lse: torch.Tensor | None = None, need_lse: bool = True,
              stream: torch.cuda.Stream | None = None):
     """Attention forward on the GPU: returns (o, lse).
@@ -171,23 +207,29 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     H_KV = k.shape[1]
     if k.shape != (B, H_KV, N, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B, H_KV, N, d] with q's B, N, d")
+    _same_device(q, k, v)
     if o is None:
         o = torch.empty_like(q)
-    elif o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous():
-        raise ValueError("o must be a contiguous bf16 tensor shaped like q")
+    _check_out("o", o, q.shape, torch.bfloat16, q.device)
     if lse is None and need_lse:
         lse = torch.empty((B, H_Q, N), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.shape != (B, H_Q, N) or lse.dtype != torch.float32
-                            or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 [B, H_Q, N] tensor")
+    if lse is not None:
+        _check_out("lse", lse, (B, H_Q, N), torch.float32, q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         rc = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                           lse.data_ptr() if lse is not None else None,
                           B, H_Q, H_KV, N, d, int(bool(causal)),
-                          _mapping_id(mapping), _stream_handle(stream, q.device))
+                          _mapping_id(mapping, causal), _stream_handle(stream, q.device))
     _check(rc, "attn_fwd")
     return o, lse
+
+
+def _same_device(*ts):
+    dev = ts[0].device
+    for t in ts[1:]:
+        if t.device != dev:
+            raise ValueError(f"every input must be on {dev}; found one on {t.device}")
 
 
 def _check_bf16(name, t):
@@ -212,7 +254,7 @@ def attn_split_chunk(N_kv: int, num_splits: int) -> int:
 
 
 def attn_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                   causal: bool = False, num_splits: int = 1, mapping=3,
+                   causal: bool = False, num_splits: int = 1, mapping=None,
                    o: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                    o_ws: torch.Tensor | None = None, lse_ws: torch.Tensor | None = None,
                    need_lse: bool = True, stream: torch.cuda.Stream | None = None):
@@ -227,22 +269,22 @@ def attn_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     H_KV, N_kv = k.shape[1], k.shape[2]
     if k.shape != (B, H_KV, N_kv, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B, H_KV, N_kv, d] with q's B and d")
+    _same_device(q, k, v)
     S = int(num_splits)
     if o is None:
         o = torch.empty_like(q)
-    elif o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous():
-        raise ValueError("o must be a contiguous bf16 tensor shaped like q")
+    _check_out("o", o, q.shape, torch.bfloat16, q.device)
     if lse is None and need_lse:
         lse = torch.empty((B, H_Q, N_q), dtype=torch.float32, device=q.device)
     if lse is not None:
-        _check_f32("lse", lse, (B, H_Q, N_q))
+        _check_out("lse", lse, (B, H_Q, N_q), torch.float32, q.device)
     if S > 1:
         if o_ws is None:
             o_ws = torch.empty((S, B, H_Q, N_q, d), dtype=torch.float32, device=q.device)
         if lse_ws is None:
             lse_ws = torch.empty((S, B, H_Q, N_q), dtype=torch.float32, device=q.device)
-        _check_f32("o_ws", o_ws, (S, B, H_Q, N_q, d))
-        _check_f32("lse_ws", lse_ws, (S, B, H_Q, N_q))
+        _check_out("o_ws", o_ws, (S, B, H_Q, N_q, d), torch.float32, q.device)
+        _check_out("lse_ws", lse_ws, (S, B, H_Q, N_q), torch.float32, q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         rc = lib.attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
@@ -250,7 +292,7 @@ def attn_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                 B, H_Q, H_KV, N_q, N_kv, d, int(bool(causal)), S,
                                 o_ws.data_ptr() if S > 1 else None,
                                 lse_ws.data_ptr() if S > 1 else None,
-                                _mapping_id(mapping), _stream_handle(stream, q.device))
+                                _mapping_id(mapping, causal), _stream_handle(stream, q.device))
     _check(rc, "attn_fwd_split")
     return o, lse
 
@@ -265,15 +307,14 @@ def attn_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,
     S, B, H_Q, N_q, d = o_parts.shape
     _check_f32("o_parts", o_parts, (S, B, H_Q, N_q, d))
     _check_f32("lse_parts", lse_parts, (S, B, H_Q, N_q))
+    _same_device(o_parts, lse_parts)
     if o is None:
         o = torch.empty((B, H_Q, N_q, d), dtype=torch.bfloat16, device=o_parts.device)
-    _check_bf16("o", o)
-    if o.shape != (B, H_Q, N_q, d):
-        raise ValueError("o must be [B, H_Q, N_q, d]")
+    _check_out("o", o, (B, H_Q, N_q, d), torch.bfloat16, o_parts.device)
     if lse is None and need_lse:
         lse = torch.empty((B, H_Q, N_q), dtype=torch.float32, device=o_parts.device)
     if lse is not None:
-        _check_f32("lse", lse, (B, H_Q, N_q))
+        _check_out("lse", lse, (B, H_Q, N_q), torch.float32, o_parts.device)
     lib = load_library()
     with torch.cuda.device(o_parts.device):
         rc = lib.attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, B, H_Q, N_q, d,
@@ -284,7 +325,7 @@ def attn_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,
 
 
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-             dout: torch.Tensor, lse: torch.Tensor, causal: bool = False, mapping=3,
+             dout: torch.Tensor, lse: torch.Tensor, causal: bool = False, mapping=None,
              dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
              dv: torch.Tensor | None = None, ws: torch.Tensor | None = None,
              stream: torch.cuda.Stream | None = None):
@@ -302,22 +343,21 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if o.shape != q.shape or dout.shape != q.shape:
         raise ValueError("o and dout must be shaped like q")
     _check_f32("lse", lse, (B, H_Q, N))
+    _same_device(q, k, v, o, dout, lse)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        _check_bf16(name, t)
-        if t.shape != ref.shape:
-            raise ValueError(f"{name} must have shape {tuple(ref.shape)}")
+        _check_out(name, t, ref.shape, torch.bfloat16, q.device)
     if ws is None:
         ws = torch.empty((2, B, H_Q, N), dtype=torch.float32, device=q.device)
-    _check_f32("ws", ws, (2, B, H_Q, N))
+    _check_out("ws", ws, (2, B, H_Q, N), torch.float32, q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                           dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                           dv.data_ptr(), ws.data_ptr(), B, H_Q, H_KV, N, d,
-                          int(bool(causal)), _mapping_id(mapping),
+                          int(bool(causal)), _mapping_id(mapping, causal),
                           _stream_handle(stream, q.device))
     _check(rc, "attn_bwd")
     return dq, dk, dv
@@ -351,12 +391,12 @@ def cac_gemm(a: torch.Tensor, b: torch.Tensor, mapping=3, group_m: int = 0,
     L, M, K = a3.shape
     if b3.shape[0] != L or b3.shape[2] != K:
         raise ValueError("b must be [L, N, K] with a's L and K")
+    _same_device(a3, b3)
     N = b3.shape[1]
     shape = (M, N) if squeeze else (L, M, N)
     if c is None:
         c = torch.empty(shape, dtype=torch.bfloat16, device=a.device)
-    elif (tuple(c.shape) != shape or c.dtype != torch.bfloat16 or not c.is_contiguous()):
-        raise ValueError(f"c must be a contiguous bf16 tensor of shape {shape}")
+    _check_out("c", c, shape, torch.bfloat16, a.device)
     lib = load_library()
     with torch.cuda.device(a.device):
         rc = lib.cac_gemm(a3.data_ptr(), b3.data_ptr(), c.data_ptr(), L, M, N, K,
@@ -404,9 +444,13 @@ def attn_probe_placement(mapping, B: int, H_Q: int, H_KV: int, N: int,
     W = num_workgroups(B, H_Q, N)
     if out is None:
         out = torch.empty((W, 4), dtype=torch.int32, device=device)
+    if not isinstance(out, torch.Tensor) or not out.is_cuda:
+        raise ValueError("out must be a GPU tensor")
+    _check_out("out", out, (W, 4), torch.int32, out.device)
     lib = load_library()
     with torch.cuda.device(out.device):
-        rc = lib.attn_probe_placement(_mapping_id(mapping), B, H_Q, H_KV, N,
+        rc = lib.attn_probe_placement(_mapping_id(mapping if mapping is not None else 3),
+                                      B, H_Q, H_KV, N,
                                       out.data_ptr(),
                                       _stream_handle(stream, out.device))
     _check(rc, "attn_probe_placement")

@@ -218,9 +218,13 @@ int attn_block_m(void);
 
 /*
  * attn_num_xcd: XCDs of the current device (8 on MI355X in SPX mode), the
- * count attn_fwd swizzles over.  The environment variable ATTN_NUM_XCD (an
- * integer 1..64) overrides it.  Returns the count (>= 1) or a negative
- * ATTN_E_* code (ATTN_E_NO_DEVICE without a GPU).
+ * count attn_fwd swizzles over.
+ *
+ * Passage: digest page, §2 Q1 (the dispatcher hands workgroup w to XCD
+ * w mod X) and §7 Figure 11, where this count is the NUM_XCD constant of
+ * the swizzle.  Read from hipDeviceAttributeNumberOfXccs.  The environment
+ * variable ATTN_NUM_XCD (an integer 1..64) overrides it.  Returns the count
+ * (>= 1) or a negative ATTN_E_* code (ATTN_E_NO_DEVICE without a GPU).
  */
 int attn_num_xcd(void);
 
@@ -238,8 +242,15 @@ int attn_num_xcd(void);
 int attn_probe_placement(int mapping, int B, int H_Q, int H_KV, int N,
                          int32_t* dev_out, void* stream);
 
-/* Text for an ATTN_E_* code; for ATTN_E_HIP, the calling thread's last HIP
-   error.  The pointer stays valid until the next call on the same thread. */
+/*
+ * attn_strerror: text for an ATTN_E_* code; for ATTN_E_HIP, the calling
+ * thread's last HIP error.  The pointer stays valid until the next call on
+ * the same thread.
+ *
+ * Passage: none.  The pages define no host interface; this is the error
+ * reporting of the C boundary around the kernels (plain int codes, no
+ * exceptions across the ABI).  Unknown codes return a generic text.
+ */
 const char* attn_strerror(int code);
 
 #ifdef __cplusplus

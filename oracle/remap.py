@@ -47,8 +47,8 @@ order with a row block's heads adjacent; with G = 1 it is the base mode with
 m reversed).
 
 Parity status: pinned.  On the domain where the pages print formulas (one
-batch, X dividing H_Q, X dividing W) tests/test_wg_map_oracle.py checks
-equality with those formulas restated from the pages, and the invariants the
+batch, X dividing H_Q, X dividing W) tests/test_remap_oracle.py checks
+the dispatch order those formulas produce, and the invariants the
 pages state (one ACC per XCD, 16 heads per XCD for Naive Block-first at
 H_Q=128, Figure 10's 8-head / 4-XCD example) everywhere else.
 """

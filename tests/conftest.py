@@ -16,3 +16,33 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def repo_root():
     return ROOT
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Worst forward parity figures of the run, raw and beyond the bf16
+    output rounding, printed (also under -q) and written to
+    gpurun_out/parity_report.json when any forward comparison ran."""
+    import json
+    try:
+        from tests import gpu_util
+    except Exception:
+        return
+    rows = gpu_util.REPORT
+    if not rows:
+        return
+    worst = {key: max(rows, key=lambda r: r[key])
+             for key in ("o_max_abs_raw", "o_max_abs_beyond_bf16", "o_rel_l2", "lse_max_abs")}
+    tr = terminalreporter
+    tr.write_line(f"forward parity over {len(rows)} comparisons (bars: O max|err| beyond "
+                  f"bf16 rounding <= {gpu_util.O_MAX_ABS}, rel-L2 <= {gpu_util.O_REL_L2}, "
+                  f"lse <= {gpu_util.LSE_MAX_ABS}):")
+    for key, r in worst.items():
+        tr.write_line(f"  worst {key} = {r[key]:.3e}  ({r['what']})")
+    out = os.path.join(ROOT, "gpurun_out")
+    try:
+        os.makedirs(out, exist_ok=True)
+        with open(os.path.join(out, "parity_report.json"), "w") as f:
+            json.dump({"worst": {k: {"value": r[k], "case": r["what"]} for k, r in worst.items()},
+                       "comparisons": rows}, f, indent=1)
+    except OSError:
+        pass

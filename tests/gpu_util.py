@@ -30,6 +30,12 @@ O_REL_L2 = 5e-3
 LSE_MAX_ABS = 1e-3
 
 
+# Every forward comparison of this session: (what, raw max|err|, max|err|
+# beyond the bf16 output rounding, rel-L2, lse max|err|).  tests/conftest.py
+# prints the worst of each at the end of the run and writes them as JSON.
+REPORT: list[dict] = []
+
+
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
@@ -58,6 +64,8 @@ def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
     raw_max = float(raw.max()) if raw.size else 0.0
     say(f"  {what}: O max|err| beyond bf16 rounding={max_abs:.3e} (raw {raw_max:.3e}) "
         f"relL2={rel:.3e} lse max|err|={lse_err:.3e}")
+    REPORT.append({"what": what, "o_max_abs_raw": raw_max, "o_max_abs_beyond_bf16": max_abs,
+                   "o_rel_l2": rel, "lse_max_abs": lse_err})
     assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
     assert max_abs <= O_MAX_ABS, f"{what}: O max|err| {max_abs}"
     assert rel <= O_REL_L2, f"{what}: O rel-L2 {rel}"

@@ -279,3 +279,42 @@ def test_gemm_argument_errors(lib):
     assert lib.cac_gemm_map(3, 1, 256, 256, 0, 0, 0, out.ctypes.data) == c["ATTN_E_SHAPE"]
     assert lib.cac_gemm_map(4, 1, 256, 256, 0, 0, 8, out.ctypes.data) == c["ATTN_E_MAPPING"]
     assert lib.cac_gemm_map(3, 1, 256, 256, 0, 0, 8, None) == c["ATTN_E_NULL"]
+
+
+# ---- caller-given outputs and workspaces are checked before any launch -----
+def test_check_out_rejects_every_bad_buffer():
+    import torch
+    dev = torch.device("cuda", 0)          # constructing it needs no GPU
+    ok_shape = (1, 2, 3, 8)
+    bad = [
+        ("host tensor", torch.empty(ok_shape, dtype=torch.bfloat16), "must be on"),
+        ("wrong shape", torch.empty((1, 2, 3, 16), dtype=torch.bfloat16), "of shape"),
+        ("wrong dtype", torch.empty(ok_shape, dtype=torch.float16), "of shape"),
+        ("not a tensor", np.zeros(ok_shape), "torch.Tensor"),
+    ]
+    for what, t, msg in bad:
+        with pytest.raises(ValueError, match=msg):
+            attn._check_out("o", t, ok_shape, torch.bfloat16, dev)
+
+
+def test_check_out_rejects_non_contiguous_and_another_device():
+    import torch
+    t = torch.empty((6, 4), dtype=torch.float32).t()
+    with pytest.raises(ValueError, match="contiguous"):
+        attn._check_out("ws", t, (4, 6), torch.float32, torch.device("cuda", 0))
+    with pytest.raises(ValueError, match="must be on cuda:1"):
+        attn._check_out("ws", t.contiguous(), (4, 6), torch.float32, torch.device("cuda", 1))
+
+
+def test_probe_placement_rejects_a_host_buffer(lib):
+    import torch
+    W = attn.num_workgroups(1, 8, 1024)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        attn.attn_probe_placement(3, 1, 8, 8, 1024, out=torch.empty((W, 4), dtype=torch.int32))
+
+
+def test_default_mapping_depends_on_the_mask():
+    assert attn._mapping_id(None, causal=False) == attn.DEFAULT_MAPPING == 3
+    assert attn._mapping_id(None, causal=True) == attn.DEFAULT_CAUSAL_MAPPING == 3 | 4 | 8
+    assert attn._mapping_id("swizzled_head_first", causal=True) == 3
+    assert attn._mapping_id(5, causal=True) == 5

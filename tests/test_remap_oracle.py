@@ -1,12 +1,18 @@
-"""The integer remap oracle against the pages' formulas and invariants (CPU).
+"""The integer remap oracle against what the pages state and show (CPU).
 
-Formulas restated from "Optimizing Attention on GPUs by Exploiting GPU
-Architectural NUMA Effects" (digest page):
-* §2 Q2 / §7 Figure 11 (Swizzled Head-first, one batch, X | H_Q):
-  head  = (w mod X) * (H_Q / X) + floor(w / (X * M))
-  block = floor((w mod (X * M)) / X)
-* §7 Figure 3 (chiplet swizzle, X | W):
-  new_id = (w mod X) * (W / X) + floor(w / X)
+"Optimizing Attention on GPUs by Exploiting GPU Architectural NUMA Effects"
+(digest page):
+* §2 Q1: the dispatcher hands workgroup w to XCD w mod X.
+* §2 Q2 and §6 step 5: Swizzled Head-first gives one XCD a whole ACC (every
+  row block of one head) before it moves to the next, and gives each XCD its
+  own run of consecutive heads; §3 Figure 10 shows it for 8 heads, 128 row
+  blocks and 4 XCDs (golden fixture).
+* §7 Figure 3: the chiplet swizzle hands each XCD one contiguous run of the
+  logical workgroup order.
+* §4 "6 minimum checks" item 3: Naive Block-first puts 16 heads on each XCD
+  at H_Q = 128 (golden fixture).
+These are checked as properties of the dispatch order (what the k-th
+workgroup each XCD receives computes), not by re-typing the printed code.
 """
 import os
 import random
@@ -26,14 +32,6 @@ CONFIGS = [
     (1, 64, 8, 8192), (1, 64, 8, 32768), (1, 64, 8, 131072),
     (2, 32, 4, 32768), (2, 12, 12, 32768), (1, 12, 12, 32768),
 ]
-
-
-def pages_shf(w, H_Q, M, X):
-    return (w % X) * (H_Q // X) + w // (X * M), (w % (X * M)) // X
-
-
-def pages_swizzle(w, W, X):
-    return (w % X) * (W // X) + w // X
 
 
 def _read_golden(name):
@@ -73,24 +71,40 @@ def test_every_mode_is_a_bijection(mode):
             assert 0 <= b < B and 0 <= h < H_Q and 0 <= m < M
 
 
-def test_shf_equals_pages_formula_single_batch():
+def _per_xcd_sequence(mode, B, H_Q, N, X, G=1):
+    """Per XCD, what its k-th workgroup (ids x, x + X, x + 2X, ...) computes."""
+    W = oracle.num_workgroups(B, H_Q, N)
+    seq = defaultdict(list)
+    for w in range(W):
+        seq[oracle.xcd_of(w, X)].append(oracle.wg_map(mode, w, B, H_Q, N, X, G=G))
+    return seq
+
+
+def test_shf_dispatch_order_single_batch():
+    """One batch, X | H_Q: XCD x receives heads x*H_Q/X .. (x+1)*H_Q/X - 1,
+    one head at a time (a whole ACC before the next), each head's row blocks
+    in order, and no other XCD receives any of them."""
     for H_Q, M, X in [(128, 64, 8), (16, 8, 8), (64, 3, 8), (8, 128, 4),
                       (128, 1024, 8), (24, 5, 4), (6, 7, 2), (5, 9, 1)]:
-        for w in range(H_Q * M):
-            b, h, m = oracle.wg_map(SHF, w, 1, H_Q, M * 128, X)
-            assert b == 0 and (h, m) == pages_shf(w, H_Q, M, X), (H_Q, M, X, w)
+        seq = _per_xcd_sequence(SHF, 1, H_Q, M * 128, X)
+        hpx = H_Q // X
+        for x in range(X):
+            expect = [(0, h, m) for h in range(x * hpx, (x + 1) * hpx) for m in range(M)]
+            assert seq[x] == expect, (H_Q, M, X, x)
 
 
-def test_sbf_equals_pages_swizzle_then_block_first():
+def test_sbf_dispatch_order_is_contiguous_runs_of_block_first():
+    """X | W: XCD x receives the x-th contiguous run of W/X workgroups of the
+    block-first order (batch outermost, then row block, heads fastest)."""
     for B, H_Q, M, X in [(1, 128, 64, 8), (2, 16, 8, 8), (1, 12, 2, 8),
                          (3, 4, 2, 4), (1, 8, 128, 4)]:
         W = B * H_Q * M
         assert W % X == 0
-        for w in range(W):
-            L = pages_swizzle(w, W, X)
-            b, r = divmod(L, H_Q * M)
-            expect = (b, r % H_Q, r // H_Q)
-            assert oracle.wg_map(SBF, w, B, H_Q, M * 128, X) == expect
+        order = [(b, h, m) for b in range(B) for m in range(M) for h in range(H_Q)]
+        seq = _per_xcd_sequence(SBF, B, H_Q, M * 128, X)
+        n = W // X
+        for x in range(X):
+            assert seq[x] == order[x * n:(x + 1) * n], (B, H_Q, M, X, x)
 
 
 def _acc(b, h, H_Q, H_KV):
@@ -200,19 +214,18 @@ def test_figure10_worked_example_golden():
     assert got == golden
 
 
-def test_printed_batch_term_needs_the_batch_outer_reading():
-    """As printed, the per-batch id is the linear id divided by the batch
-    count; with two batches that is not a bijection, which is why the oracle
-    puts the batch outermost."""
+def test_batch_outer_reading_keeps_each_batch_whole_per_xcd_run():
+    """With B > 1 the oracle puts the batch outermost (the printed per-batch
+    id is not a bijection for B = 2); under SHF with X | H_Q every XCD then
+    serves batch 0's heads before batch 1's, and each (batch, head) whole."""
     B, H_Q, M, X = 2, 16, 8, 8
-    seen = set()
-    for w in range(B * H_Q * M):
-        wpb = w // B
-        head = (wpb % X) * (H_Q // X) + wpb // (X * M)
-        block = (wpb % (X * M)) // X
-        batch = (w // (M * H_Q)) % B
-        seen.add((batch, head, block))
-    assert len(seen) < B * H_Q * M
+    seq = _per_xcd_sequence(SHF, B, H_Q, M * 128, X)
+    for x, items in seq.items():
+        assert [b for b, _, _ in items] == sorted(b for b, _, _ in items)
+        heads = defaultdict(set)
+        for b, h, m in items:
+            heads[(b, h)].add(m)
+        assert all(ms == set(range(M)) for ms in heads.values())
 
 
 # ---- LONGEST_FIRST (causal-aware order; not on the pages) -------------------
