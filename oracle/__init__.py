@@ -8,14 +8,16 @@ from .sdpa import attention, attention_head_rows, attention_sampled, kv_head
 from .split import causal_offset, merge, partial_attention, partial_head_rows
 from .backward import attention_backward, backward_key_rows, backward_query_rows
 from .gemm import cac_tile_table, gemm
-from .remap import (NBF, NHF, SBF, SHF, LONGEST_FIRST, MODE_NAMES, chiplet_swizzle,
-                     num_workgroups, row_blocks, wg_map, wg_table, xcd_of)
+from .remap import (NBF, NHF, SBF, SHF, LONGEST_FIRST, BALANCED_SPLIT, MODE_NAMES,
+                     acc_is_split, chiplet_swizzle, folded, num_workgroups, row_blocks,
+                     slice_starts, wg_map, wg_table, xcd_of)
 
 __all__ = [
     "attention", "attention_head_rows", "attention_sampled", "kv_head",
     "causal_offset", "merge", "partial_attention", "partial_head_rows",
     "attention_backward", "backward_key_rows", "backward_query_rows",
     "cac_tile_table", "gemm",
-    "NBF", "NHF", "SBF", "SHF", "LONGEST_FIRST", "MODE_NAMES", "chiplet_swizzle",
-    "num_workgroups", "row_blocks", "wg_map", "wg_table", "xcd_of",
+    "NBF", "NHF", "SBF", "SHF", "LONGEST_FIRST", "BALANCED_SPLIT", "MODE_NAMES",
+    "acc_is_split", "chiplet_swizzle", "folded", "num_workgroups", "row_blocks",
+    "slice_starts", "wg_map", "wg_table", "xcd_of",
 ]

@@ -46,6 +46,22 @@ base mode is kept; within each ACC the row blocks run in non-increasing
 order with a row block's heads adjacent; with G = 1 it is the base mode with
 m reversed).
 
+Added (not on the pages): BALANCED_SPLIT, the fallback made work-balanced
+for causal attention (the digest's §7 implementation notes leave the
+fallback open; the commentary page raises H_Q = 12 over 8 XCDs without a
+remedy).  It changes Swizzled Head-first only (other modes ignore it).  The
+balanced slices stay as they are, so every XCD still takes its ACCs in one
+contiguous run; but an ACC that a slice boundary splits takes its
+(row block, head) units in folded order: the longest-first list with its
+first unit, then its last, then its second, then its second-to-last, ...
+Under a causal mask row block m carries work that grows linearly with m, so
+each consecutive pair of the folded list carries the same work, and the
+pieces of a split ACC on two XCDs carry work in proportion to their unit
+counts.  Pinned by properties (bijection; identical to the mode without the
+bit wherever no ACC is split and for every other base mode; the ACC-per-XCD
+structure unchanged; per-XCD causal work within one row block's work of the
+mean, where the plain slices are off by up to 16% at H_Q = 12).
+
 Parity status: pinned.  On the domain where the pages print formulas (one
 batch, X dividing H_Q, X dividing W) tests/test_remap_oracle.py checks
 the dispatch order those formulas produce, and the invariants the
@@ -53,6 +69,8 @@ pages state (one ACC per XCD, 16 heads per XCD for Naive Block-first at
 H_Q=128, Figure 10's 8-head / 4-XCD example) everywhere else.
 """
 from __future__ import annotations
+
+import functools
 
 NBF, NHF, SBF, SHF = 0, 1, 2, 3
 MODE_NAMES = {NBF: "naive_block_first", NHF: "naive_head_first",
@@ -96,19 +114,71 @@ def _decode(L: int, H_Q: int, M: int, head_first: bool):
 LONGEST_FIRST = 4
 
 
+# Added to a mode: work-balanced fallback for Swizzled Head-first (not on
+# the pages): an ACC split between XCDs takes its units in folded order.
+BALANCED_SPLIT = 8
+
+
+def slice_starts(W: int, X: int):
+    """First logical index of each XCD's slice (and W at the end)."""
+    starts = [0]
+    for x in range(X):
+        starts.append(starts[-1] + W // X + (1 if x < W % X else 0))
+    return starts
+
+
+def _slice_of(P: int, starts) -> int:
+    x = 0
+    while starts[x + 1] <= P:
+        x += 1
+    return x
+
+
+def acc_is_split(a: int, G: int, M: int, W: int, X: int) -> bool:
+    """Whether ACC a (logical range [a*G*M, (a+1)*G*M)) meets two slices."""
+    starts = slice_starts(W, X)
+    return _slice_of(a * G * M, starts) != _slice_of((a + 1) * G * M - 1, starts)
+
+
+def folded(units):
+    """First, last, second, second-to-last, ... of a list."""
+    out, i, j = [], 0, len(units) - 1
+    while i <= j:
+        out.append(units[i])
+        if i != j:
+            out.append(units[j])
+        i, j = i + 1, j - 1
+    return out
+
+
+@functools.lru_cache(maxsize=64)
+def _folded_units(M: int, G: int):
+    """(row block, head within the KV group) of an ACC's units: the
+    longest-first list (row block M-1 .. 0, a row block's G heads adjacent)
+    in folded order."""
+    return tuple(folded([(M - 1 - md, hg) for md in range(M) for hg in range(G)]))
+
+
 def wg_map(mode: int, w: int, B: int, H_Q: int, N: int, X: int,
            block_m: int = 128, G: int = 1):
     """(b, h_q, m) computed by linear workgroup id ``w`` under ``mode``
-    (0..3, optionally + LONGEST_FIRST); G = query heads per KV group."""
+    (0..3, optionally + LONGEST_FIRST and/or BALANCED_SPLIT); G = query heads
+    per KV group."""
     M = row_blocks(N, block_m)
     W = B * H_Q * M
     if not 0 <= w < W:
         raise ValueError("workgroup id out of range")
-    if not 0 <= mode <= 7 or H_Q % G:
+    if not 0 <= mode <= 15 or H_Q % G:
         raise ValueError("unknown mapping mode or G")
     base, longest_first = mode & 3, bool(mode & LONGEST_FIRST)
     L = chiplet_swizzle(w, W, X) if base in (SBF, SHF) else w
     head_first = base in (NHF, SHF)
+    if base == SHF and mode & BALANCED_SPLIT:
+        a, s = divmod(L, G * M)            # global ACC (b, kv) and position in it
+        if acc_is_split(a, G, M, W, X):
+            b, kv = divmod(a, H_Q // G)
+            m, hg = _folded_units(M, G)[s]
+            return b, kv * G + hg, m
     if longest_first and head_first:
         b, r = divmod(L, H_Q * M)
         acc, s = divmod(r, G * M)

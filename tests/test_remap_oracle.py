@@ -292,4 +292,120 @@ def test_longest_first_keeps_acc_per_xcd_and_orders_each_acc():
 
 def test_longest_first_rejects_bad_mode():
     with pytest.raises(ValueError):
-        oracle.wg_map(8, 0, 1, 8, 1024, 8)
+        oracle.wg_map(-1, 0, 1, 8, 1024, 8)
+
+
+# ---- BALANCED_SPLIT (work-balanced fallback; not on the pages) -------------
+BAL = oracle.BALANCED_SPLIT
+
+
+def _causal_unit_work(m, N, bm):
+    """(query, key) pairs of row block m under a top-left causal mask."""
+    lo, hi = m * bm, min((m + 1) * bm, N)
+    return (hi * (hi + 1) - lo * (lo + 1)) // 2
+
+
+def _bal_shapes(n=150, seed=11):
+    rng = random.Random(seed)
+    out = [(1, 12, 12, 32768, 8, 256), (2, 12, 12, 32768, 8, 256), (1, 32, 4, 32768, 8, 256),
+           (1, 6, 2, 4096, 8, 256), (3, 5, 5, 1000, 8, 128), (1, 8, 1, 8192, 8, 256)]
+    for _ in range(n):
+        H_KV, G, B, M = rng.randint(1, 12), rng.randint(1, 4), rng.randint(1, 3), rng.randint(1, 30)
+        bm = rng.choice([128, 256])
+        N = max(M * bm - rng.choice([0, 0, 1, 77]), 1)
+        out.append((B, H_KV * G, H_KV, N, rng.choice([2, 4, 8]), bm))
+    return out
+
+
+def test_balanced_split_is_a_bijection_in_every_mode():
+    for B, H_Q, H_KV, N, X, bm in _bal_shapes(60):
+        G = H_Q // H_KV
+        for mode in range(8, 16):
+            tab = oracle.wg_table(mode, B, H_Q, N, X, block_m=bm, G=G)
+            assert len(set(tab)) == len(tab) == oracle.num_workgroups(B, H_Q, N, bm), mode
+
+
+def test_balanced_split_changes_only_the_split_accs_of_shf():
+    """Other base modes ignore the bit; under SHF a workgroup of an ACC that
+    no slice boundary splits computes what it computes without the bit."""
+    for B, H_Q, H_KV, N, X, bm in _bal_shapes(80, seed=12):
+        G = H_Q // H_KV
+        M = oracle.row_blocks(N, bm)
+        W = B * H_Q * M
+        for base in (0, 1, 2, 4, 5, 6):
+            assert (oracle.wg_table(base | BAL, B, H_Q, N, X, bm, G)
+                    == oracle.wg_table(base, B, H_Q, N, X, bm, G))
+        for lf in (0, oracle.LONGEST_FIRST):
+            plain = oracle.wg_table(SHF | lf, B, H_Q, N, X, bm, G)
+            bal = oracle.wg_table(SHF | lf | BAL, B, H_Q, N, X, bm, G)
+            for w in range(W):
+                a = oracle.chiplet_swizzle(w, W, X) // (G * M)
+                if not oracle.acc_is_split(a, G, M, W, X):
+                    assert bal[w] == plain[w]
+
+
+def test_balanced_split_keeps_each_acc_on_its_xcds():
+    """The XCDs of every ACC are those of plain SHF (each XCD's ACCs one
+    contiguous run; an ACC on at most 2 XCDs when there are at least X ACCs),
+    and a split ACC's piece on each XCD has the unit count it had."""
+    for B, H_Q, H_KV, N, X, bm in _bal_shapes(80, seed=13):
+        G = H_Q // H_KV
+        per_plain, per_bal = defaultdict(list), defaultdict(list)
+        for w, ((b, h, _), (b2, h2, _)) in enumerate(zip(
+                oracle.wg_table(SHF | 4, B, H_Q, N, X, bm, G),
+                oracle.wg_table(SHF | 4 | BAL, B, H_Q, N, X, bm, G))):
+            per_plain[w % X].append(_acc(b, h, H_Q, H_KV))
+            per_bal[w % X].append(_acc(b2, h2, H_Q, H_KV))
+        for x in per_plain:
+            assert per_bal[x] == per_plain[x]
+            assert per_bal[x] == sorted(per_bal[x])
+        if B * H_KV >= X:
+            spans = defaultdict(set)
+            for x, accs in per_bal.items():
+                for a in accs:
+                    spans[a].add(x)
+            assert all(len(s) <= 2 for s in spans.values())
+
+
+def test_balanced_split_per_xcd_causal_work_within_a_row_block_of_the_mean():
+    """Per-XCD causal work (query-key pairs) is within one row block's work
+    of the mean when N is a multiple of the row-block height, and within two
+    for ragged N (the last row block breaks the linear work of the fold)."""
+    worst_exact = worst_ragged = 0.0
+    for B, H_Q, H_KV, N, X, bm in _bal_shapes(150, seed=14):
+        G = H_Q // H_KV
+        M = oracle.row_blocks(N, bm)
+        unit_max = max(_causal_unit_work(m, N, bm) for m in range(M))
+        work = [0] * X
+        for w, (b, h, m) in enumerate(oracle.wg_table(SHF | 4 | BAL, B, H_Q, N, X, bm, G)):
+            work[w % X] += _causal_unit_work(m, N, bm)
+        mean = sum(work) / X
+        dev = max(abs(x - mean) for x in work) / unit_max
+        if N % bm == 0:
+            worst_exact = max(worst_exact, dev)
+        else:
+            worst_ragged = max(worst_ragged, dev)
+    assert worst_exact <= 1.0 and worst_ragged <= 2.0, (worst_exact, worst_ragged)
+
+
+def test_balanced_split_c4_prime_numbers():
+    """B=1, H=12, N=32K, 256-row blocks, 8 XCDs: plain slices leave the
+    heaviest XCD 16.7% above the mean causal work (the piece holding the
+    long row blocks of a split ACC); the folded pieces balance it exactly."""
+    N, bm = 32768, 256
+    for mode, expect in ((SHF | 4, 1.1667), (SHF, 1.1667), (SHF | 4 | BAL, 1.0), (SHF | BAL, 1.0)):
+        work = [0] * 8
+        for w, (b, h, m) in enumerate(oracle.wg_table(mode, 1, 12, N, 8, bm, 1)):
+            work[w % 8] += _causal_unit_work(m, N, bm)
+        assert round(max(work) / (sum(work) / 8), 4) == expect, mode
+
+
+def test_folded_order_small_example():
+    assert oracle.folded([0, 1, 2, 3, 4]) == [0, 4, 1, 3, 2]
+    assert oracle.folded([0, 1, 2, 3]) == [0, 3, 1, 2]
+    assert oracle.folded([]) == []
+
+
+def test_balanced_split_rejects_bad_mode():
+    with pytest.raises(ValueError):
+        oracle.wg_map(16, 0, 1, 8, 1024, 8)
