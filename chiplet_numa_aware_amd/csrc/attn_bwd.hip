@@ -78,7 +78,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
   if ((rows + 3) / 4 >= (uint64_t(1) << 31)) return ATTN_E_SHAPE;
   rc = check_head_dim(N, d);
   if (rc != ATTN_OK) return rc;
-  if (mapping < 0 || mapping > 7) return ATTN_E_MAPPING;
+  if (mapping < 0 || mapping > kMaxMapping) return ATTN_E_MAPPING;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(ws))
     return ATTN_E_ALIGN;

@@ -40,7 +40,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   if (rc != ATTN_OK) return rc;
   rc = check_head_dim(N_kv, d);
   if (rc != ATTN_OK) return rc;
-  if (mapping < 0 || mapping > 7) return ATTN_E_MAPPING;
+  if (mapping < 0 || mapping > kMaxMapping) return ATTN_E_MAPPING;
   if (num_splits > 1 && (!o_ws || !lse_ws)) return ATTN_E_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (lse && !aligned16(lse)) || (num_splits > 1 && (!aligned16(o_ws) || !aligned16(lse_ws))))

@@ -42,7 +42,7 @@ int attn_wg_map(int mapping, int B, int H_Q, int H_KV, int N, int num_xcd,
   int rc = check_shape(B, H_Q, H_KV, N, &M, &W);
   if (rc != ATTN_OK) return rc;
   if (num_xcd < 1) return ATTN_E_SHAPE;
-  if (mapping < 0 || mapping > 7) return ATTN_E_MAPPING;
+  if (mapping < 0 || mapping > kMaxMapping) return ATTN_E_MAPPING;
   for (int w = 0; w < W; ++w) {
     const WgCoord c = wg_map(mapping, (uint32_t)w, (uint32_t)B, (uint32_t)H_Q,
                              (uint32_t)M, (uint32_t)num_xcd, (uint32_t)(H_Q / H_KV));
@@ -67,7 +67,7 @@ int attn_probe_placement(int mapping, int B, int H_Q, int H_KV, int N,
   int M = 0, W = 0;
   int rc = check_shape(B, H_Q, H_KV, N, &M, &W);
   if (rc != ATTN_OK) return rc;
-  if (mapping < 0 || mapping > 7) return ATTN_E_MAPPING;
+  if (mapping < 0 || mapping > kMaxMapping) return ATTN_E_MAPPING;
   if (!aligned16(dev_out)) return ATTN_E_ALIGN;
   int X = 1;
   rc = resolve_xcd(&X);

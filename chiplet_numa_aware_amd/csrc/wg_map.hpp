@@ -29,7 +29,19 @@
 // Batch is the outermost index in both orders.  Slices are balanced (their
 // lengths differ by at most one), which is also the fallback when X does not
 // divide the number of ACCs: every XCD still walks its ACCs in one run and an
-// ACC is split only where a slice boundary falls inside it.
+// ACC is split only where a slice boundary falls inside it.  The pages leave
+// that fallback open (digest §7, key implementation details, item 1; the
+// commentary page's H_Q = 12 example).
+// A fourth bit, not on the pages, balances the fallback's work:
+//   bit 3  balanced split (swizzled head-first only; other modes ignore it):
+//                   an ACC that a slice boundary splits takes its (row block,
+//                   head) units in folded order, i.e. the longest-first list
+//                   taken first, last, second, second-to-last, ...  Under a
+//                   causal mask the work of row block m grows linearly with
+//                   m, so consecutive units of the folded list pair up into
+//                   equal work, and each XCD's piece of a split ACC carries
+//                   work in proportion to its unit count.  Whole ACCs keep
+//                   the order of bits 0-2.
 #pragma once
 
 #include <stdint.h>
@@ -48,7 +60,9 @@ enum Mapping : int {
   kSwizzledBlockFirst = 2,
   kSwizzledHeadFirst = 3,
   kLongestFirst = 4,  // bit, combined with any of the above
+  kBalancedSplit = 8, // bit, acts on kSwizzledHeadFirst only
 };
+constexpr int kMaxMapping = 15;
 
 constexpr int kBlockM = 256;  // query rows per workgroup (row-block height)
 
@@ -65,17 +79,40 @@ ATTN_HD uint32_t chiplet_slice_index(uint32_t w, uint32_t W, uint32_t X) {
   return x * base + (x < extra ? x : extra) + w / X;
 }
 
+// XCD slice holding logical position P < W (the inverse of the balanced
+// slicing: the first W mod X slices hold one more position).
+ATTN_HD uint32_t slice_of(uint32_t P, uint32_t W, uint32_t X) {
+  const uint32_t base = W / X;
+  const uint32_t big = (W % X) * (base + 1);  // positions in the longer slices
+  return P < big ? P / (base + 1) : W % X + (P - big) / base;
+}
+
 // All arguments are assumed validated: W = B*H_Q*M < 2^31, X >= 1, w < W,
 // G (query heads per ACC) >= 1 divides H_Q.
 ATTN_HD WgCoord wg_map(int mapping, uint32_t w, uint32_t B, uint32_t H_Q,
                        uint32_t M, uint32_t X, uint32_t G) {
   const uint32_t per_batch = H_Q * M;
-  const uint32_t L =
-      (mapping & 2) ? chiplet_slice_index(w, B * per_batch, X) : w;
+  const uint32_t W = B * per_batch;
+  const uint32_t L = (mapping & 2) ? chiplet_slice_index(w, W, X) : w;
   WgCoord c;
   c.b = L / per_batch;
   const uint32_t r = L - c.b * per_batch;
   uint32_t m;
+  if ((mapping & 3) == kSwizzledHeadFirst && (mapping & kBalancedSplit)) {
+    const uint32_t U = G * M;  // units of one ACC; ACC a holds [a U, a U + U)
+    const uint32_t a = L / U;
+    if (slice_of(a * U, W, X) != slice_of(a * U + U - 1, W, X)) {
+      const uint32_t s = L - a * U;
+      // folded position s -> index u of the longest-first list (row block
+      // M-1-u/G, head u mod G of the group)
+      const uint32_t u = (s & 1u) ? U - 1u - (s >> 1) : (s >> 1);
+      const uint32_t md = u / G;
+      const uint32_t acc_in_batch = r / U;
+      c.h = acc_in_batch * G + (u - md * G);
+      c.m = M - 1u - md;
+      return c;
+    }
+  }
   if ((mapping & 1) && (mapping & kLongestFirst)) {  // ACC, block, head
     const uint32_t acc = r / (G * M);
     const uint32_t s = r - acc * (G * M);

@@ -81,7 +81,7 @@ def predict_hit(B: int, H_Q: int, H_KV: int, N: int, d: int, causal: bool,
 
 
 def best_mapping(B: int, H_Q: int, H_KV: int, N: int, d: int, causal: bool,
-                 candidates=(3, 7, 1, 2, 0), **kw) -> int:
+                 candidates=(3, 7, 15, 1, 2, 0), **kw) -> int:
     """The candidate mapping with the highest predicted hit rate (ties go to
     the earlier candidate)."""
     scores = [(predict_hit(B, H_Q, H_KV, N, d, causal, m, **kw), -i, m)

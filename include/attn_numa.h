@@ -37,7 +37,7 @@ extern "C" {
 #define ATTN_E_SHAPE (-2)       /* B, H_Q, H_KV or N <= 0, H_Q % H_KV != 0,
                                    or a size beyond the 32-bit limits below */
 #define ATTN_E_HEAD_DIM (-3)    /* d <= 0, d > 128 or d % 8 != 0 */
-#define ATTN_E_MAPPING (-4)     /* mapping not in 0..7 */
+#define ATTN_E_MAPPING (-4)     /* mapping not in 0..15 */
 #define ATTN_E_ALIGN (-5)       /* a device pointer is not 16-byte aligned */
 #define ATTN_E_HIP (-6)         /* HIP runtime or launch error */
 #define ATTN_E_NO_DEVICE (-7)   /* no HIP device is visible */
@@ -54,6 +54,16 @@ extern "C" {
    of a causal ACC then stay close together in the K/V stream, which keeps
    the swizzled head-first L2 hit rate up (measured in the design notes). */
 #define ATTN_MAP_LONGEST_FIRST 4
+/* Added to ATTN_MAP_SWIZZLED_HEAD_FIRST (ignored by the other modes): the
+   work-balanced fallback.  The pages leave open what happens when the XCD
+   count does not divide the ACC count (digest §7, key implementation
+   details, item 1; the commentary page's H_Q = 12 example).  The balanced
+   slices still give every XCD one contiguous run of ACCs; an ACC that a
+   slice boundary splits takes its (row block, head) units in folded order
+   (longest, shortest, second longest, ...), so that under a causal mask
+   each XCD's share of the work is within one row block of the mean.
+   Whole ACCs keep the order the other bits give them. */
+#define ATTN_MAP_BALANCED_SPLIT 8
 
 /*
  * attn_fwd: attention forward pass.
@@ -73,8 +83,9 @@ extern "C" {
  *        64-wide tile, else a 128-wide one); B*H_Q*ceil(N/256) < 2^31 and
  *        N*d*2 <= 2^31 - 2^16 bytes per head
  *   causal  0: every key; 1: query row i sees keys 0..i (top-left aligned)
- *   mapping ATTN_MAP_* (0..3), optionally | ATTN_MAP_LONGEST_FIRST; the XCD
- *          count used is attn_num_xcd()
+ *   mapping ATTN_MAP_* (0..3), optionally | ATTN_MAP_LONGEST_FIRST and/or
+ *          | ATTN_MAP_BALANCED_SPLIT (0..15); the XCD count used is
+ *          attn_num_xcd()
  *   stream  hipStream_t or NULL
  *
  * Arithmetic: bf16 inputs, fp32 scores, softmax statistics and accumulators;
@@ -171,7 +182,7 @@ int attn_merge(const float* o_parts, const float* lse_parts, int num_splits,
  *               lse * log2(e), then D; overwritten
  *   B, H_Q, H_KV, N, d, causal   as attn_fwd (the same mask); also
  *               B*H_Q*ceil(N/128) < 2^31
- *   mapping     ATTN_MAP_* (0..7) as attn_fwd: the dK/dV kernel maps
+ *   mapping     ATTN_MAP_* (0..15) as attn_fwd: the dK/dV kernel maps
  *               (batch, KV head, 128-key block) with the remap's row blocks
  *               counted from the last key block (the fewest query rows under
  *               a causal mask), the dQ kernel (batch, query head, 128-row block)

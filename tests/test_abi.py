@@ -59,7 +59,7 @@ def test_head_size_limit(lib):
     assert _fwd(lib, N=limit // 256 + 1, mapping=3, **kw) == c["ATTN_E_SHAPE"]
     # At the limit the shape passes and the (invalid) mapping is reported:
     # validation ends before anything could launch on the fake pointers.
-    assert _fwd(lib, N=limit // 256, mapping=8, **kw) == c["ATTN_E_MAPPING"]
+    assert _fwd(lib, N=limit // 256, mapping=16, **kw) == c["ATTN_E_MAPPING"]
 
 
 def test_strerror_covers_every_code(lib):
@@ -93,7 +93,7 @@ def test_fwd_argument_errors(lib):
         assert _fwd(lib, d=d) == c["ATTN_E_HEAD_DIM"], d
     # one head larger than 2 GiB does not fit a buffer resource
     assert _fwd(lib, N=1 << 23, d=128, H_Q=1, H_KV=1) == c["ATTN_E_SHAPE"]
-    for m in (-1, 8, 99):
+    for m in (-1, 16, 99):
         assert _fwd(lib, mapping=m) == c["ATTN_E_MAPPING"]
     for kw in ({"q": FAKE + 2}, {"k": FAKE + 8}, {"v": FAKE + 1},
                {"o": FAKE + 4}, {"lse": FAKE + 4}):
@@ -106,10 +106,10 @@ def test_wg_map_and_probe_argument_errors(lib):
     assert lib.attn_wg_map(3, 1, 8, 8, 1024, 8, None) == c["ATTN_E_NULL"]
     assert lib.attn_wg_map(3, 1, 8, 3, 1024, 8, buf.ctypes.data) == c["ATTN_E_SHAPE"]
     assert lib.attn_wg_map(3, 1, 8, 8, 1024, 0, buf.ctypes.data) == c["ATTN_E_SHAPE"]
-    assert lib.attn_wg_map(8, 1, 8, 8, 1024, 8, buf.ctypes.data) == c["ATTN_E_MAPPING"]
+    assert lib.attn_wg_map(16, 1, 8, 8, 1024, 8, buf.ctypes.data) == c["ATTN_E_MAPPING"]
     assert lib.attn_probe_placement(3, 1, 8, 8, 1024, None, None) == c["ATTN_E_NULL"]
     assert lib.attn_probe_placement(3, 0, 8, 8, 1024, FAKE, None) == c["ATTN_E_SHAPE"]
-    assert lib.attn_probe_placement(8, 1, 8, 8, 1024, FAKE, None) == c["ATTN_E_MAPPING"]
+    assert lib.attn_probe_placement(16, 1, 8, 8, 1024, FAKE, None) == c["ATTN_E_MAPPING"]
     assert lib.attn_probe_placement(3, 1, 8, 8, 1024, FAKE + 4, None) == c["ATTN_E_ALIGN"]
 
 
@@ -126,7 +126,7 @@ def _shapes():
     return shapes
 
 
-@pytest.mark.parametrize("mode", list(range(8)))
+@pytest.mark.parametrize("mode", list(range(16)))
 def test_host_wg_map_equals_oracle(mode):
     for B, H_Q, H_KV, N, X in _shapes():
         got = attn.attn_wg_map(mode, B, H_Q, H_KV, N, X)
@@ -143,7 +143,7 @@ def test_host_wg_map_equals_oracle(mode):
 
 
 def test_host_wg_map_is_bijection_on_headline_shape():
-    for mode in range(8):
+    for mode in range(16):
         t = attn.attn_wg_map(mode, 1, 128, 128, 131072, 8).astype(np.int64)
         key = (t[:, 0] * 128 + t[:, 1]) * 1024 + t[:, 2]
         assert np.unique(key).size == t.shape[0] == 128 * (131072 // attn.BLOCK_M)
@@ -189,7 +189,7 @@ def test_split_and_merge_argument_errors(lib):
                {"B": 1 << 12, "H_Q": 1 << 10, "N_q": 256, "S": 1 << 10}):
         assert _split(lib, **kw) == c["ATTN_E_SHAPE"], kw
     assert _split(lib, d=12) == c["ATTN_E_HEAD_DIM"]
-    assert _split(lib, mapping=8) == c["ATTN_E_MAPPING"]
+    assert _split(lib, mapping=16) == c["ATTN_E_MAPPING"]
     assert _split(lib, o_ws=FAKE + 4) == c["ATTN_E_ALIGN"]
     m = lambda **kw: lib.attn_merge(kw.get("op", FAKE), kw.get("lp", FAKE), kw.get("S", 2),
                                     kw.get("B", 1), kw.get("H", 2), kw.get("N", 3),
@@ -211,7 +211,7 @@ def test_bwd_argument_errors(lib):
         ptrs = [kw.get(n, FAKE) for n in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws")]
         return lib.attn_bwd(*ptrs, kw.get("B", 1), kw.get("H_Q", 4), kw.get("H_KV", 2),
                             kw.get("N", 300), kw.get("d", 128), kw.get("causal", 1),
-                            kw.get("mapping", 8 if "mapping_ok" not in kw else 3), None)
+                            kw.get("mapping", 16 if "mapping_ok" not in kw else 3), None)
 
     for n in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws"):
         assert b(**{n: None}) == c["ATTN_E_NULL"], n
@@ -221,7 +221,7 @@ def test_bwd_argument_errors(lib):
         assert b(**kw) == c["ATTN_E_SHAPE"], kw
     for d in (0, 12, 136):
         assert b(d=d) == c["ATTN_E_HEAD_DIM"], d
-    assert b() == c["ATTN_E_MAPPING"]          # mapping 8
+    assert b() == c["ATTN_E_MAPPING"]          # mapping 16
     assert b(mapping=-1) == c["ATTN_E_MAPPING"]
     for n in ("q", "dout", "lse", "dk", "ws"):
         assert b(mapping_ok=1, **{n: FAKE + 4}) == c["ATTN_E_ALIGN"], n

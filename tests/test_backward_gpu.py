@@ -53,7 +53,7 @@ def test_backward_bitwise_identical_across_mappings(causal):
     q, k, v, dout = grad_inputs(2, 8, 2, 1000, 128, seed=910)
     o, lse = attn.attn_fwd(q, k, v, causal=causal)
     ref = None
-    for mapping in range(8):
+    for mapping in range(16):
         dq, dk, dv = attn.attn_bwd(q, k, v, o, dout, lse, causal=causal, mapping=mapping)
         torch.cuda.synchronize()
         if ref is None:

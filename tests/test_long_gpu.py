@@ -1,6 +1,6 @@
 """Full-size workloads: the HIP forward pass in the launch configuration the
 benchmark times, checked on seeded sampled (batch, head, row) sets against the
-fp64 oracle row by row, plus bitwise invariance across the four mappings.
+fp64 oracle row by row, plus bitwise invariance across the mapping modes.
 
 Workloads (bf16 N(0,1) inputs, d=128 unless stated):
   MHA B=1 H_Q=H_KV=128, N in {8192, 32768, 131072}, non-causal and causal;
@@ -62,7 +62,9 @@ def test_long_sampled_parity(cfg):
     name, B, H_Q, H_KV, N, d, causal, seed = cfg
     say(f"case {name}: B={B} H_Q={H_Q} H_KV={H_KV} N={N} d={d} causal={causal}")
     q, k, v = inputs.make_qkv(B, H_Q, H_KV, N, d, seed=seed, device="cuda")
-    o, lse = attn.attn_fwd(q, k, v, causal=causal, mapping=3)
+    # The binding's default mapping: swizzled head-first, and for causal
+    # workloads with longest first and balanced splits (mode 15).
+    o, lse = attn.attn_fwd(q, k, v, causal=causal)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(lse).all())
     _sampled_check(q, k, v, o, lse, causal, name)
@@ -70,13 +72,25 @@ def test_long_sampled_parity(cfg):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("cfg", [LONG[2], LONG[7], LONG[11]], ids=lambda c: c[0])
-def test_mappings_bitwise_identical(cfg):
+INVARIANCE = [
+    # (config, modes compared with mode 0)
+    (LONG[2], (1, 2, 3)),
+    (LONG[7], (1, 2, 3, 7, 15)),
+    # the longest-first modes at the longest causal shape
+    (LONG[5], (4, 5, 6, 7, 15)),
+    # the fallback shape (12 ACCs over 8 XCDs): every mode, including the
+    # balanced split (8-15), whose folded order changes 4 of the 12 ACCs
+    (LONG[11], tuple(range(1, 16))),
+]
+
+
+@pytest.mark.parametrize("cfg,modes", INVARIANCE, ids=lambda c: c[0] if isinstance(c, tuple) and isinstance(c[0], str) else None)
+def test_mappings_bitwise_identical(cfg, modes):
     name, B, H_Q, H_KV, N, d, causal, seed = cfg
-    say(f"case mapping invariance {name}")
+    say(f"case mapping invariance {name} modes {modes}")
     q, k, v = inputs.make_qkv(B, H_Q, H_KV, N, d, seed=seed, device="cuda")
     o0, l0 = attn.attn_fwd(q, k, v, causal=causal, mapping=0)
-    for m in (1, 2, 3):
+    for m in modes:
         o, l = attn.attn_fwd(q, k, v, causal=causal, mapping=m)
         torch.cuda.synchronize()
         assert torch.equal(o, o0) and torch.equal(l, l0), m

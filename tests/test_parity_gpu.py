@@ -34,7 +34,7 @@ def test_c1_full_oracle_every_mapping():
     q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
     o_ref, lse_ref = _oracle(q, k, v, False)
     outs = []
-    for mapping in range(8):
+    for mapping in range(16):
         o, lse = _run(q, k, v, False, mapping)
         assert_close(f64(o), f64(lse), o_ref, lse_ref, f"C1 mapping {mapping}")
         outs.append((o.clone(), lse.clone()))
@@ -69,9 +69,16 @@ def test_small_shapes_full_oracle(shape):
     q, k, v = inputs.make_qkv(B, H_Q, H_KV, N, d, seed=7 + N + d, device="cpu")
     q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
     o_ref, lse_ref = _oracle(q, k, v, causal)
-    for mapping in (0, 3):
+    # 15 = swizzled head-first + longest first + balanced split: several of
+    # these shapes have ACCs that a slice boundary splits (e.g. H=12, N=1100:
+    # 5 row blocks per ACC, 7-8 workgroups per XCD).
+    outs = []
+    for mapping in (0, 3, 15):
         o, lse = _run(q, k, v, causal, mapping)
         assert_close(f64(o), f64(lse), o_ref, lse_ref, f"{shape} mapping {mapping}")
+        outs.append((o, lse))
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -33,7 +33,7 @@ def test_probe_matches_host_table_and_dispatch_model(shape):
     B, H_Q, H_KV, N = shape
     X = attn.attn_num_xcd()
     say(f"case probe {shape} X={X}")
-    for mode in range(8):
+    for mode in range(16):
         out = attn.attn_probe_placement(mode, B, H_Q, H_KV, N)
         torch.cuda.synchronize()
         out = out.cpu().numpy()
@@ -45,7 +45,7 @@ def test_probe_matches_host_table_and_dispatch_model(shape):
         for r in range(X):
             assert np.unique(xcc[w % X == r]).size == 1, (mode, r)
         assert np.unique(xcc).size == min(X, out.shape[0])
-        if mode in (3, 7) and (B * H_KV) % X == 0:
+        if mode & 3 == 3 and (B * H_KV) % X == 0:
             acc = out[:, 1] * H_KV + out[:, 2] // (H_Q // H_KV)
             per = defaultdict(set)
             for a, x in zip(acc, xcc):
