@@ -91,3 +91,26 @@ def test_gemm_full_size_sampled_rows(mapping):
     ridx = torch.as_tensor(rows, device="cuda")
     check_gemm(f64(c[0].index_select(0, ridx)), f64(a[0].index_select(0, ridx)), f64(b[0]),
                f"tall GEMM sampled rows, mapping {mapping}")
+
+
+@pytest.mark.parametrize("shape", [(8, 16384, 1024, 4096), (1, 16384, 16384, 16384)],
+                         ids=["batched_L8_16k_1k_4k", "square_16k"])
+def test_gemm_full_size_batched_and_square(shape):
+    """The benchmark's batched (L=8) and square shapes in their launch
+    configuration (swizzled cluster map, default cluster): seeded rows of C of
+    every batch against the oracle under the rigorous bound (32 rows per
+    batch for L=8, 48 rows for the square)."""
+    L, M, N, K = shape
+    say(f"case GEMM full size L={L} M={M} N={N} K={K}")
+    a, b = _ab(L, M, N, K, seed=1000)
+    c = attn.cac_gemm(a, b, mapping=3)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(1234))
+    n = 32 if L > 1 else 48
+    for l in range(L):
+        rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.choice(M, n - 4, replace=False)]))
+        ridx = torch.as_tensor(rows, device="cuda")
+        check_gemm(f64(c[l].index_select(0, ridx)), f64(a[l].index_select(0, ridx)), f64(b[l]),
+                   f"GEMM L={L} M={M} N={N} K={K} batch {l} sampled rows")
+    del a, b, c
+    torch.cuda.empty_cache()
