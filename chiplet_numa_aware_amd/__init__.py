@@ -7,6 +7,7 @@ entry points have the names of the C ABI in include/attn_numa.h:
 
 * ``attn_fwd(q, k, v, causal=False, mapping=None, o=None, lse=None)``
 * ``attn_fwd_split(q, k, v, causal=False, num_splits=1, mapping=None, ...)``
+* ``attn_fwd_split_noalloc(q, k, v, o, lse=None, causal=False, num_splits=1, ...)``
 * ``attn_split_chunk(N_kv, num_splits)``
 * ``attn_merge(o_parts, lse_parts, o=None, lse=None)``
 * ``attn_bwd(q, k, v, o, dout, lse, causal=False, mapping=None, ...)``
@@ -35,7 +36,8 @@ import numpy as np
 import torch  # first, so the library binds to the HIP runtime torch loaded
 
 __all__ = [
-    "AttnError", "attn_fwd", "attn_fwd_split", "attn_split_chunk", "attn_merge", "attn_bwd",
+    "AttnError", "attn_fwd", "attn_fwd_split", "attn_fwd_split_noalloc", "SCRATCH_BYTES",
+    "attn_split_chunk", "attn_merge", "attn_bwd",
     "cac_gemm", "cac_gemm_map", "cac_gemm_tile", "CAC_MAPPINGS",
     "attn_wg_map", "attn_num_xcd", "attn_block_m",
     "attn_probe_placement", "attn_strerror", "library_path", "load_library",
@@ -97,6 +99,8 @@ def load_library():
     lib.attn_fwd.restype = i32
     lib.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp] + [i32] * 8 + [vp, vp, i32, vp]
     lib.attn_fwd_split.restype = i32
+    lib.attn_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp] + [i32] * 9 + [vp]
+    lib.attn_fwd_split_noalloc.restype = i32
     lib.attn_split_chunk.argtypes = [i32, i32]
     lib.attn_split_chunk.restype = i32
     lib.attn_merge.argtypes = [vp, vp] + [i32] * 5 + [vp, vp, vp]
@@ -294,6 +298,41 @@ def attn_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                 lse_ws.data_ptr() if S > 1 else None,
                                 _mapping_id(mapping, causal), _stream_handle(stream, q.device))
     _check(rc, "attn_fwd_split")
+    return o, lse
+
+
+# ATTN_SCRATCH_BYTES of include/attn_numa.h: the fixed device scratch of
+# attn_fwd_split_noalloc.
+SCRATCH_BYTES = 32 * 1024 * 1024
+
+
+def attn_fwd_split_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           o: torch.Tensor, lse: torch.Tensor | None = None,
+                           causal: bool = False, num_splits: int = 1, mapping=None,
+                           stream: torch.cuda.Stream | None = None):
+    """attn_fwd_split with its split partials in the library's fixed device
+    scratch (ATTN_SCRATCH_BYTES per GPU) instead of a workspace: for callers
+    that cannot allocate.  The caller passes the outputs o (bf16, shaped
+    like q) and optionally lse (fp32 [B, H_Q, N_q]); nothing is allocated.
+    Calls that overlap on one GPU share the scratch and race."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(name, t)
+    B, H_Q, N_q, d = q.shape
+    H_KV, N_kv = k.shape[1], k.shape[2]
+    if k.shape != (B, H_KV, N_kv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H_KV, N_kv, d] with q's B and d")
+    _same_device(q, k, v)
+    _check_out("o", o, q.shape, torch.bfloat16, q.device)
+    if lse is not None:
+        _check_out("lse", lse, (B, H_Q, N_q), torch.float32, q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        rc = lib.attn_fwd_split_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        lse.data_ptr() if lse is not None else None,
+                                        B, H_Q, H_KV, N_q, N_kv, d, int(bool(causal)),
+                                        int(num_splits), _mapping_id(mapping, causal),
+                                        _stream_handle(stream, q.device))
+    _check(rc, "attn_fwd_split_noalloc")
     return o, lse
 
 

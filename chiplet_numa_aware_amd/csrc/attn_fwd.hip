@@ -1,11 +1,14 @@
 // C ABI of the attention forward pass (attn_fwd, attn_fwd_split,
-// attn_split_chunk, attn_merge in include/attn_numa.h): argument validation,
-// the split-KV and packing choices, and the launches on the caller's stream.
-// No entry point allocates or synchronises.
+// attn_fwd_split_noalloc, attn_split_chunk, attn_merge in
+// include/attn_numa.h): argument validation, the split-KV and packing
+// choices, and the launches on the caller's stream.  No entry point
+// allocates or synchronises; attn_fwd_split_noalloc keeps its split partials
+// in the library's fixed device array.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/attn_numa.h"
 #include "attn_fwd_kernel.hpp"
@@ -77,6 +80,39 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
 }
 
 
+// Fixed device scratch of attn_fwd_split_noalloc: the split partials (O of
+// each split, then its lse) of one call.  Each GPU the library runs on holds
+// its own copy until the process ends.  In host code `scratch` is only a
+// stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+static __device__ __align__(256) float scratch[ATTN_SCRATCH_BYTES / sizeof(float)];
+
+std::once_flag g_scratch_once[kMaxDevices];
+float* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of this device's scratch (the current device), or null with
+// the HIP error in *err.
+float* device_scratch(hipError_t* err) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? static_cast<float*>(p) : nullptr;
+  });
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+
+// Bytes of scratch a split call needs: O partials, then lse partials from the
+// next 256-byte boundary.
+uint64_t scratch_lse_offset(uint64_t rows, int d) { return (rows * (uint64_t)d * 4 + 255) / 256 * 256; }
+
 }  // namespace
 }  // namespace attn_numa
 
@@ -97,6 +133,29 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o,
                    float* lse_ws, int mapping, void* stream) {
   return fwd_impl(q, k, v, o, lse, B, H_Q, H_KV, N_q, N_kv, d, causal,
                   num_splits, o_ws, lse_ws, mapping, N_q < kBlockM, stream);
+}
+
+int attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o,
+                           float* lse, int B, int H_Q, int H_KV, int N_q, int N_kv,
+                           int d, int causal, int num_splits, int mapping, void* stream) {
+  if (num_splits <= 1)
+    return fwd_impl(q, k, v, o, lse, B, H_Q, H_KV, N_q, N_kv, d, causal, num_splits,
+                    nullptr, nullptr, mapping, N_q < kBlockM, stream);
+  // Size check first, before any device query: rows of all splits, with the
+  // shape's own limits checked by fwd_impl below.
+  if (B <= 0 || H_Q <= 0 || N_q <= 0) return ATTN_E_SHAPE;
+  if (d <= 0 || d > 128 || (d % 8) != 0) return ATTN_E_HEAD_DIM;
+  const uint64_t rows = (uint64_t)num_splits * (uint64_t)B * (uint64_t)H_Q * (uint64_t)N_q;
+  const uint64_t lse_off = scratch_lse_offset(rows, d);
+  if (lse_off + rows * 4 > (uint64_t)ATTN_SCRATCH_BYTES) return ATTN_E_SCRATCH;
+  if (!q || !k || !v || !o) return ATTN_E_NULL;
+  int devs = 0;
+  if (hipGetDeviceCount(&devs) != hipSuccess || devs <= 0) return ATTN_E_NO_DEVICE;
+  hipError_t e = hipSuccess;
+  float* base = device_scratch(&e);
+  if (!base) return hip_fail(e, "attn_fwd_split_noalloc scratch address");
+  return fwd_impl(q, k, v, o, lse, B, H_Q, H_KV, N_q, N_kv, d, causal, num_splits, base,
+                  base + lse_off / 4, mapping, N_q < kBlockM, stream);
 }
 
 int attn_split_chunk(int N_kv, int num_splits) {

@@ -88,11 +88,14 @@ const char* attn_strerror(int code) {
       return "bad shape (B, H_Q, H_KV, N must be > 0, H_Q % H_KV == 0, "
              "B*H_Q*ceil(N/256) < 2^31, N*d*2 <= 2^31 - 2^16, num_xcd >= 1)";
     case ATTN_E_HEAD_DIM: return "unsupported head dim (need 8 <= d <= 128, d % 8 == 0)";
-    case ATTN_E_MAPPING: return "mapping must be 0..7";
+    case ATTN_E_MAPPING: return "mapping out of range (attention 0..15, cac_gemm 0..3)";
     case ATTN_E_ALIGN: return "device pointer not 16-byte aligned";
     case ATTN_E_HIP:
       return g_err_text[0] ? g_err_text : "HIP runtime error";
     case ATTN_E_NO_DEVICE: return "no HIP device visible";
+    case ATTN_E_SCRATCH:
+      return "the split workspace would exceed the library's fixed device scratch "
+             "(ATTN_SCRATCH_BYTES); use attn_fwd_split with a caller workspace";
     default: return "unknown error code";
   }
 }

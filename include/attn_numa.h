@@ -41,6 +41,8 @@ extern "C" {
 #define ATTN_E_ALIGN (-5)       /* a device pointer is not 16-byte aligned */
 #define ATTN_E_HIP (-6)         /* HIP runtime or launch error */
 #define ATTN_E_NO_DEVICE (-7)   /* no HIP device is visible */
+#define ATTN_E_SCRATCH (-8)     /* attn_fwd_split_noalloc: the workspace would
+                                   not fit ATTN_SCRATCH_BYTES */
 
 /* Workgroup remap modes (digest page §3 before/after table, §5). */
 #define ATTN_MAP_NAIVE_BLOCK_FIRST 0    /* id order, heads fastest */
@@ -135,6 +137,35 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o,
                    float* lse, int B, int H_Q, int H_KV, int N_q, int N_kv,
                    int d, int causal, int num_splits, float* o_ws,
                    float* lse_ws, int mapping, void* stream);
+
+/*
+ * attn_fwd_split_noalloc: attn_fwd_split without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The same computation and kernels as attn_fwd_split (results are
+ * bit-identical to it); the split partials (o_ws, lse_ws of attn_fwd_split)
+ * live in a fixed device array of ATTN_SCRATCH_BYTES that the library owns:
+ * each GPU it runs on holds one such array from the first call on that GPU
+ * until the process ends.  The call itself allocates nothing (no hipMalloc,
+ * no allocating library routine).
+ *
+ *   q, k, v, o, lse, B, H_Q, H_KV, N_q, N_kv, d, causal, num_splits,
+ *   mapping, stream   as attn_fwd_split.
+ * Needs num_splits * B * H_Q * N_q * (d + 1) * 4 bytes (rounded up to 256
+ * between the two parts) <= ATTN_SCRATCH_BYTES when num_splits > 1; larger
+ * calls return ATTN_E_SCRATCH before touching the device.  Every call
+ * overwrites all of the scratch it uses before reading it, so nothing has to
+ * be cleared between calls; calls that overlap on one GPU (e.g. on two
+ * streams) share the array and race, so the caller serialises them.
+ * Errors: as attn_fwd_split; ATTN_E_SCRATCH; ATTN_E_HIP also when the
+ * array's device address cannot be obtained.
+ */
+#define ATTN_SCRATCH_BYTES (32 * 1024 * 1024)
+int attn_fwd_split_noalloc(const void* q, const void* k, const void* v,
+                           void* o, float* lse, int B, int H_Q, int H_KV,
+                           int N_q, int N_kv, int d, int causal,
+                           int num_splits, int mapping, void* stream);
 
 /*
  * attn_split_chunk: keys per split for attn_fwd_split, ceil(N_kv /

@@ -34,7 +34,8 @@ def _declared_codes():
 
 def test_library_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_split", "attn_split_chunk", "attn_merge",
+    assert set(names) == {"attn_fwd", "attn_fwd_split", "attn_fwd_split_noalloc",
+                          "attn_split_chunk", "attn_merge",
                           "attn_bwd", "attn_wg_map", "attn_num_xcd", "attn_block_m",
                           "attn_probe_placement", "attn_strerror"}
     for n in names:
@@ -318,3 +319,23 @@ def test_default_mapping_depends_on_the_mask():
     assert attn._mapping_id(None, causal=True) == attn.DEFAULT_CAUSAL_MAPPING == 3 | 4 | 8
     assert attn._mapping_id("swizzled_head_first", causal=True) == 3
     assert attn._mapping_id(5, causal=True) == 5
+
+
+def test_noalloc_rejects_oversize_before_touching_a_device(lib):
+    """attn_fwd_split_noalloc checks the scratch size first: a call whose
+    split partials exceed ATTN_SCRATCH_BYTES returns ATTN_E_SCRATCH with no
+    device query (there is no GPU here), and bad shapes are still reported."""
+    c = _declared_codes()
+    text = open(HEADER).read()
+    limit = int(re.search(r"#define ATTN_SCRATCH_BYTES \((\d+) \* 1024 \* 1024\)", text).group(1)) << 20
+    assert limit == attn.SCRATCH_BYTES
+
+    def n(B=4, H_Q=32, H_KV=8, N_q=64, N_kv=4096, d=128, S=64):
+        return lib.attn_fwd_split_noalloc(FAKE, FAKE, FAKE, FAKE, None, B, H_Q, H_KV, N_q,
+                                          N_kv, d, 1, S, 3, None)
+    assert 64 * 4 * 32 * 64 * 129 * 4 > limit
+    assert n() == c["ATTN_E_SCRATCH"]
+    assert n(B=0) == c["ATTN_E_SHAPE"]
+    assert n(d=12) == c["ATTN_E_HEAD_DIM"]
+    # fits: validation passes the size check and stops at the missing GPU
+    assert n(S=8, N_q=1) == c["ATTN_E_NO_DEVICE"]
