@@ -73,10 +73,38 @@ METRIC = "attn fwd TFLOP/s + % bf16 MFMA peak + L2 hit %, MHA H=128 N=128K d=128
 PEAK_BF16_TFLOPS = 2500.0
 _BASE_NAMES = ["naive_block_first", "naive_head_first",
                "swizzled_block_first", "swizzled_head_first"]
-# Mode ids 0..7: the pages' four modes, and each + 4 (longest first).
+# Mode ids 0..15: the pages' four modes, each + 4 (longest first), and each
+# of those + 8 (balanced split, which changes swizzled head-first only).
 MODE_NAMES = _BASE_NAMES + [n + "_longest_first" for n in _BASE_NAMES]
-SWEEP_MODES = (0, 1, 2, 3, 7)
+MODE_NAMES = MODE_NAMES + [n + "_balanced_split" for n in MODE_NAMES]
+SWEEP_MODES = (0, 1, 2, 3, 7, 15)
 PROFILE_MODES = SWEEP_MODES  # one dispatch each, in this order, per profile pass
+
+# Vector-ALU roofline of the online softmax.  Per (query, key) score the
+# softmax needs one FMA (scale, minus the running max), one exp2, one add
+# (row sum) and half a conversion to bf16 (two scores per instruction).  A
+# wave64 fp32 FMA, add or conversion issues in 4 SIMD cycles (16 lanes per
+# cycle: 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz = 78.6 TFLOP/s, half
+# the packed 157.3), v_exp_f32 in 8 (measured: two issue slots).  So one
+# wave's 64 scores take 4 + 8 + 4 + 4/2 = 18 SIMD cycles.
+SIMDS = 256 * 4
+CLOCK_HZ = 2.4e9
+SOFTMAX_SIMD_CYCLES_PER_WAVE = {"fma": 4, "exp2": 8, "add": 4, "cvt_bf16_half": 2}
+SOFTMAX_SCORES_PER_S = SIMDS * CLOCK_HZ * 64 / sum(SOFTMAX_SIMD_CYCLES_PER_WAVE.values())
+
+
+def alu_peak_tflops(d: int) -> float:
+    """Credited TFLOP/s (4 d FLOP per score) at the softmax's vector-ALU
+    bound."""
+    return SOFTMAX_SCORES_PER_S * 4 * d / 1e12
+
+
+def mfma_peak_tflops_credited(d: int) -> float:
+    """Credited TFLOP/s at the MFMA peak: the kernel pads d to 64 or 128
+    columns, and the padding is executed but not credited."""
+    d_pad = 64 if d <= 64 else 128
+    return PEAK_BF16_TFLOPS * d / d_pad
+
 
 WORKLOADS = {
     # name: (B, H_Q, H_KV, N, d, causal)
@@ -144,6 +172,15 @@ def device_info() -> dict:
             "partition": "SPX (one device spans all 8 XCDs)" if xcd == 8 else f"{xcd} XCDs",
             "rocm": rocm, "hip": torch.version.hip,
             "host_cores": len(os.sched_getaffinity(0))}
+
+
+def emit(out: dict, args) -> None:
+    """Prints the one JSON line (and writes it to --json-out when given)."""
+    line = json.dumps(out)
+    if getattr(args, "json_out", None):
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    print(line, flush=True)
 
 
 def log(*a):
@@ -325,6 +362,10 @@ PROFILE_PASSES = {
     "write": ["WRITE_SIZE"],
     "mfma": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
              "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+    # where the non-MFMA time goes: instruction mix and waits (wave-cycles
+    # in units of 4 cycles)
+    "issue": ["SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA"],
+    "waits": ["SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY"],
 }
 
 
@@ -334,7 +375,11 @@ def profile_commands(workload: str, out: str, which: str = "fwd"):
     modes = "0,1,2,3" if which in ("gemm", "decode") else ",".join(map(str, PROFILE_MODES))
     sel = f"--workload {workload}" + ("" if which == "fwd" else f" --pass {which}")
     one = f"{bench} {sel} --steps 1 --warmup 0 --modes {modes} --no-cpu-baseline"
-    cmds = {"trace": (f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/trace -o trace -- "
+    # First the plain benchmark on the same box (its per-mode kernel times
+    # are what the summary divides the algorithmic work by), then the traces.
+    cmds = {"bench": (f"{bench} {sel} --steps 3 --warmup 1 --modes {modes} --no-cpu-baseline "
+                      f"--json-out {out}/bench.json"),
+            "trace": (f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/trace -o trace -- "
                       f"{bench} {sel} --steps 2 --warmup 1 --modes {modes} --no-cpu-baseline")}
     for name, ctrs in PROFILE_PASSES.items():
         cmds[name] = (f"rocprofv3 --pmc {' '.join(ctrs)} --output-format csv -d {out}/{name} -o {name} -- {one}")
@@ -370,6 +415,17 @@ def _recorded_commands(directory: str, workload: str, which: str = "fwd"):
     return profile_commands(workload, os.path.abspath(directory), which)
 
 
+def _same_box_bench(directory: str):
+    """Per-mode results of the bench run recorded in DIR/bench.json (the
+    profile's first command), or None."""
+    path = os.path.join(directory, "bench.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        lines = [ln for ln in f.read().splitlines() if ln.strip()]
+    return json.loads(lines[-1]).get("modes") if lines else None
+
+
 def summarize_profile(directory: str, workload: str):
     """Turns the rocprofv3 CSVs of profile_commands() into profiles/ files."""
     import csv
@@ -393,6 +449,13 @@ def summarize_profile(directory: str, workload: str):
     fe, _ = one("fetch")
     wr, _ = one("write")
     mf, mdur = one("mfma")
+    iss = None
+    if (glob.glob(os.path.join(directory, "issue", "*_counter_collection.csv"))
+            and glob.glob(os.path.join(directory, "waits", "*_counter_collection.csv"))):
+        ia, _ = one("issue")
+        ib, _ = one("waits")
+        iss = [dict(a, **b) for a, b in zip(ia, ib)] if len(ia) == len(ib) else None
+    same_box = _same_box_bench(directory)
     n_modes = len(l2)
     if not (len(fe) == len(wr) == len(mf) == n_modes == len(PROFILE_MODES)):
         raise SystemExit("expected one dispatch per mapping mode in every pass")
@@ -422,6 +485,25 @@ def summarize_profile(directory: str, workload: str):
             "clock_ghz": round(clock, 3),
             "kernel_ms_counter_run": round(durs[m] * 1e3, 2),
         }
+        entry = modes[MODE_NAMES[PROFILE_MODES[m]]]
+        if iss is not None and len(iss) == n_modes:
+            c = iss[m]
+            n_mfma = max(c["SQ_INSTS_MFMA"], 1.0)
+            entry["issue"] = {
+                # SQ_INSTS_VALU counts the MFMAs too
+                "valu_per_mfma": round((c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"]) / n_mfma, 3),
+                "salu_per_mfma": round(c["SQ_INSTS_SALU"] / n_mfma, 3),
+                "lds_per_mfma": round(c["SQ_INSTS_LDS"] / n_mfma, 3),
+                "active_inst_pct": round(100.0 * c["SQ_ACTIVE_INST_ANY"] / c["SQ_WAVE_CYCLES"], 2),
+                "wait_any_pct": round(100.0 * c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"], 2),
+                "wait_inst_any_pct": round(100.0 * c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"], 2),
+            }
+        if same_box and MODE_NAMES[PROFILE_MODES[m]] in same_box:
+            sb = same_box[MODE_NAMES[PROFILE_MODES[m]]]
+            entry["same_box_bench"] = {"kernel_ms_avg": sb["kernel_ms_avg"],
+                                       "tflops": round(flops / (sb["kernel_ms_avg"] / 1e3) / 1e12, 1),
+                                       "frac_of_peak": round(flops / (sb["kernel_ms_avg"] / 1e3) / 1e12
+                                                             / PEAK_BF16_TFLOPS, 4)}
     data = {
         "kernel": "attn_numa::attn_fwd_kernel",
         "kernel_hash": kernel_hash(),
@@ -457,7 +539,31 @@ def summarize_profile(directory: str, workload: str):
               f"write x{cal['WRITE_SIZE']:.3f}. They count L2-to-fabric traffic, so reads served by "
               f"the Infinity Cache are included.", "",
               "MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
-              "clock = GRBM_GUI_ACTIVE / 8 / kernel duration.", "", "## Commands", ""]
+              "clock = GRBM_GUI_ACTIVE / 8 / kernel duration.", ""]
+    if any("same_box_bench" in mm for mm in modes.values()):
+        lines += ["## Same-box benchmark (bench.py on the profiled box, before the profiler runs)", "",
+                  f"HIP-event mean kernel time; TFLOP/s = {flops / 1e12:.1f} TFLOP / time; fraction of "
+                  f"the {PEAK_BF16_TFLOPS:.0f} TFLOP/s bf16 peak.", "",
+                  "| mode | kernel ms | TFLOP/s | frac of peak |", "|---|---|---|---|"]
+        for name, mm in modes.items():
+            if "same_box_bench" in mm:
+                sb = mm["same_box_bench"]
+                lines.append(f"| {name} | {sb['kernel_ms_avg']:.2f} | {sb['tflops']} | {sb['frac_of_peak']} |")
+        lines.append("")
+    if any("issue" in mm for mm in modes.values()):
+        lines += ["## Where the non-MFMA time goes (SQ counters, one dispatch per mode)", "",
+                  "Instructions per MFMA (SQ_INSTS_*; VALU without the MFMAs) and the share of wave-cycles "
+                  "spent issuing (SQ_ACTIVE_INST_ANY), waiting on s_waitcnt or a barrier (SQ_WAIT_ANY) and "
+                  "waiting to issue (SQ_WAIT_INST_ANY), of SQ_WAVE_CYCLES.", "",
+                  "| mode | VALU / MFMA | SALU / MFMA | LDS / MFMA | issuing % | waitcnt+barrier % | issue-wait % |",
+                  "|---|---|---|---|---|---|---|"]
+        for name, mm in modes.items():
+            if "issue" in mm:
+                i = mm["issue"]
+                lines.append(f"| {name} | {i['valu_per_mfma']} | {i['salu_per_mfma']} | {i['lds_per_mfma']} | "
+                             f"{i['active_inst_pct']} | {i['wait_any_pct']} | {i['wait_inst_any_pct']} |")
+        lines.append("")
+    lines += ["## Commands", ""]
     lines.append("Each pass is its own process, run as `cd /tmp && export TMPDIR=/tmp && <command>` "
                  "with the repository at /root/repo; then "
                  f"`python3 bench.py --workload {workload} --summarize-profile DIR` (DIR: the directory "
@@ -639,7 +745,7 @@ def run_bwd(args, attn, inputs):
     if 0 in results and headline != 0:
         out["speedup_vs_naive_block_first"] = round(
             results[0]["kernel_ms_avg"] / head["kernel_ms_avg"], 4)
-    print(json.dumps(out), flush=True)
+    emit(out, args)
 
 
 def gemm_describe(name) -> str:
@@ -716,7 +822,7 @@ def run_gemm(args, attn, inputs):
     }
     if 0 in results and headline != 0:
         out["speedup_vs_naive_row_major"] = round(results[0]["kernel_ms_avg"] / head["kernel_ms_avg"], 4)
-    print(json.dumps(out), flush=True)
+    emit(out, args)
 
 
 def summarize_gemm_profile(directory: str, workload: str):
@@ -867,7 +973,7 @@ def run_decode(args, attn, inputs):
         "kernel_hash": kernel_hash("decode"),
         "counters_source": counters_source(args.workload, kernel_hash("decode"), "decode", counters),
     }
-    print(json.dumps(out), flush=True)
+    emit(out, args)
 
 
 def summarize_decode_profile(directory: str, workload: str):
@@ -1061,6 +1167,28 @@ def run_sweep(out_path: str):
                       "split": {name: res for name, _, _, res in split_rows}}))
 
 
+def _fwd_roofline(d: int, achieved: float, traffic):
+    """The forward kernel's binding roofline: the MFMA peak (dense bf16,
+    2.5 PFLOP/s) unless the softmax's vector-ALU bound is lower, as at
+    d <= 64 (d = 56: 1958 credited TFLOP/s against 2187 for the padded
+    MFMAs).  The other bound is reported beside it."""
+    mfma = {"bound": "mfma", "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "achieved": round(achieved, 2), "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "peak_credited_at_padded_d": round(mfma_peak_tflops_credited(d), 1)}
+    alu_peak = alu_peak_tflops(d)
+    alu = {"bound": "alu", "peak": round(alu_peak, 1), "unit": "TFLOP/s (credited)",
+           "achieved": round(achieved, 2), "frac": round(achieved / alu_peak, 4),
+           "derivation": "softmax vector work per score: fma 4 + exp2 8 + add 4 + half a bf16 "
+                         "conversion 2 SIMD cycles per wave64; 1024 SIMDs at 2.4 GHz"}
+    if alu_peak < mfma_peak_tflops_credited(d):
+        primary, other = alu, mfma
+    else:
+        primary, other = mfma, alu
+    primary = dict(primary, traffic=traffic)
+    primary["secondary"] = other
+    return primary
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -1079,6 +1207,8 @@ def main():
                          "gemm: cac_gemm (workloads gemm_*); decode: attn_fwd_split "
                          "(workloads decode_*)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--json-out", metavar="PATH",
+                    help="also write the JSON line to PATH")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--sweep", metavar="OUT_MD",
                     help="time every configuration x mapping mode, write a table")
@@ -1209,14 +1339,7 @@ def main():
         "pct_peak": round(head["pct_peak"], 2),
         "l2_hit_pct": l2_hit,
         "modes": modes_out,
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(head["kernel_tflops"], 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(head["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
-        },
+        "roofline": _fwd_roofline(d, head["kernel_tflops"], traffic),
         "kernel_hash": khash,
         "counters_source": counters_source(args.workload, khash, "fwd", counters),
         "device": device_info(),
@@ -1235,7 +1358,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host (cpu_baseline)")
         out["cpu_baseline"] = cpu_baseline(q, k, v, causal, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    emit(out, args)
 
 
 if __name__ == "__main__":

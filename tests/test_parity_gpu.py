@@ -153,6 +153,31 @@ def test_one_hot_row():
         assert torch.max(torch.abs(o[0, 0, i].float().cpu() - v[0, 0, js].float())).item() <= 1e-2
 
 
+@pytest.mark.parametrize("margin", [30.0, 300.0])
+def test_score_jump_in_a_later_tile_every_element(margin):
+    """One key row far down the sequence scores `margin` (natural units)
+    above the rest for query row i: with 30 the running max is stale by
+    ~43 log2 units when that tile arrives, with 300 by ~430, beyond the fp32
+    range of exp2.  Every element of O and lse against the oracle, causal and
+    not, and the same result under every mapping."""
+    B, H, N, d = 1, 2, 2048, 128
+    say(f"case score jump margin={margin}")
+    q, k, v = inputs.make_qkv(B, H, H, N, d, seed=91, device="cpu")
+    i, js = 1800, 1500
+    for h in range(H):
+        qi = q[0, h, i].double()
+        c = margin * math.sqrt(d) / float(qi @ qi)
+        k[0, h, js] = (c * q[0, h, i].float()).to(torch.bfloat16)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    for causal in (False, True):
+        o_ref, lse_ref = _oracle(q, k, v, causal)
+        o0, l0 = _run(q, k, v, causal, 0)
+        assert_close(f64(o0), f64(l0), o_ref, lse_ref, f"jump {margin} causal={causal}")
+        for mapping in (3, 7, 15):
+            o, lse = _run(q, k, v, causal, mapping)
+            assert torch.equal(o, o0) and torch.equal(lse, l0), mapping
+
+
 def test_lse_may_be_null_and_o_is_unchanged():
     B, H, N, d = 1, 2, 333, 128
     say("case lse=NULL")
