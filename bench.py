@@ -864,7 +864,15 @@ def summarize_gemm_profile(directory: str, workload: str):
             "clock_ghz": round(gui / 8.0 / mdur[m] / 1e9, 3),
             "kernel_ms_counter_run": round(durs[m] * 1e3, 3),
             "tflops_counter_run": round(flops / durs[m] / 1e12, 1),
+            # per GHz of the clock the dispatch ran at: tile maps compared
+            # without the power-limit clock of each run
+            "tflops_per_ghz": round(flops / durs[m] / 1e12 / (gui / 8.0 / mdur[m] / 1e9), 1),
         }
+    same_box = _same_box_bench(directory)
+    if same_box:
+        for name, mm in modes.items():
+            if name in same_box:
+                mm["same_box_bench_tflops"] = round(same_box[name]["kernel_tflops"], 1)
     trace = glob.glob(os.path.join(directory, "trace", "*_kernel_stats.csv"))
     stats = []
     if trace:
@@ -888,12 +896,13 @@ def summarize_gemm_profile(directory: str, workload: str):
                      f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} |")
     lines += ["", "(the trace mixes the 4 tile maps, 3 calls each, and torch.mm's kernels)", "",
               "## Counters per tile map (one dispatch each)", "",
-              "| tile map | L2 hit % | HBM read GB | HBM write GB | read / unique | MFMA busy % | clock GHz | ms | TFLOP/s |",
-              "|---|---|---|---|---|---|---|---|---|"]
+              "| tile map | L2 hit % | HBM read GB | HBM write GB | read / unique | MFMA busy % | clock GHz | ms | TFLOP/s | TFLOP/s per GHz | same-box bench TFLOP/s |",
+              "|---|---|---|---|---|---|---|---|---|---|---|"]
     for name, mm in modes.items():
         lines.append(f"| {name} | {mm['l2_hit_pct']} | {mm['fetch_bytes'] / 1e9:.2f} | "
                      f"{mm['write_bytes'] / 1e9:.2f} | {mm['fetch_over_unique']} | {mm['mfma_busy_pct']} | "
-                     f"{mm['clock_ghz']} | {mm['kernel_ms_counter_run']} | {mm['tflops_counter_run']} |")
+                     f"{mm['clock_ghz']} | {mm['kernel_ms_counter_run']} | {mm['tflops_counter_run']} | "
+                     f"{mm['tflops_per_ghz']} | {mm.get('same_box_bench_tflops', '')} |")
     lines += ["", f"HBM bytes: FETCH_SIZE and WRITE_SIZE scaled by a plain 1 GiB copy's counts "
               f"(read x{cal['FETCH_SIZE']:.3f}, write x{cal['WRITE_SIZE']:.3f}).", "", "## Commands", "",
               "Each pass is its own process, run as `cd /tmp && export TMPDIR=/tmp && <command>` "

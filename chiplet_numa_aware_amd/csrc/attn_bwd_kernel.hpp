@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kBwdThreads, KB == 1 ? 2 : 1) void attn_bwd_dkv_ker
   // Key block M - 1 - m: the remap's row block m counts from the block with
   // the least work under a causal mask, and for keys that is the last block
   // (it is seen by the fewest query rows).
-  const WgCoord wc = wg_map(mapping, blockIdx.x, B, H_KV, M, num_xcd, 1);
+  const WgCoord wc = wg_map_uniform(mapping, blockIdx.x, B, H_KV, M, num_xcd, 1);
   const int key0 = (M - 1 - (int)wc.m) * kBwdBlock * KB;
   int my_key[KB];
 #pragma unroll
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
-  const WgCoord wc = wg_map(mapping, blockIdx.x, B, H_Q, M, num_xcd, H_Q / H_KV);
+  const WgCoord wc = wg_map_uniform(mapping, blockIdx.x, B, H_Q, M, num_xcd, H_Q / H_KV);
   const int kvh = (int)wc.h / (H_Q / H_KV);
   const int row0 = (int)wc.m * kBwdBlock;
   const int my_row = row0 + wave * 32 + l32;

@@ -198,6 +198,19 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// The remap of this workgroup.  Its result is uniform by construction (a
+// function of the workgroup id); reading it back from the first lane states
+// that, so every address derived from it stays in scalar registers.
+__device__ __forceinline__ WgCoord wg_map_uniform(int mapping, uint32_t w, uint32_t B,
+                                                  uint32_t H_Q, uint32_t M, uint32_t X,
+                                                  uint32_t G) {
+  WgCoord c = wg_map(mapping, w, B, H_Q, M, X, G);
+  c.b = __builtin_amdgcn_readfirstlane(c.b);
+  c.h = __builtin_amdgcn_readfirstlane(c.h);
+  c.m = __builtin_amdgcn_readfirstlane(c.m);
+  return c;
+}
+
 // Pins a value to this point of the instruction stream: the empty asm is
 // ordered with the schedule barriers and the loads, so work that reads `x`
 // after it cannot be hoisted into an earlier bundle.
@@ -336,8 +349,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void attn_fwd_kernel(
   // a unit is at causal position r mod pos_mod (pos_mod = N_q).
   // The remap sees M_q * num_splits row blocks per unit: m' = split * M_q +
   // row block, so the workgroups of one key range are adjacent.
-  const WgCoord wc = wg_map(mapping, blockIdx.x, B, H_U, M_q * num_splits, num_xcd,
-                            (uint32_t)(H_U / H_KV));
+  const WgCoord wc = wg_map_uniform(mapping, blockIdx.x, B, H_U, M_q * num_splits, num_xcd,
+                                    (uint32_t)(H_U / H_KV));
   const int kvh = (int)wc.h / (H_U / H_KV);
   const int split = (int)wc.m / M_q;
   const int row0 = ((int)wc.m - split * M_q) * kBlockM;

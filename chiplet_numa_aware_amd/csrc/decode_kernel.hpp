@@ -59,7 +59,7 @@ __global__ __launch_bounds__(64, 2) void attn_decode_kernel(
 
   const int lane = threadIdx.x;
   const int g = lane >> 5, l32 = lane & 31;
-  const WgCoord wc = wg_map(mapping, blockIdx.x, B, H_U, M_q * num_splits, num_xcd,
+  const WgCoord wc = wg_map_uniform(mapping, blockIdx.x, B, H_U, M_q * num_splits, num_xcd,
                             (uint32_t)(H_U / H_KV));
   const int kvh = (int)wc.h / (H_U / H_KV);
   const int split = (int)wc.m / M_q;

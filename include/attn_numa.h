@@ -59,12 +59,14 @@ extern "C" {
 /* Added to ATTN_MAP_SWIZZLED_HEAD_FIRST (ignored by the other modes): the
    work-balanced fallback.  The pages leave open what happens when the XCD
    count does not divide the ACC count (digest §7, key implementation
-   details, item 1; the commentary page's H_Q = 12 example).  The balanced
-   slices still give every XCD one contiguous run of ACCs; an ACC that a
-   slice boundary splits takes its (row block, head) units in folded order
-   (longest, shortest, second longest, ...), so that under a causal mask
-   each XCD's share of the work is within one row block of the mean.
-   Whole ACCs keep the order the other bits give them. */
+   details, item 1; the commentary page's H_Q = 12 example).  It acts only
+   on XCDs whose slice holds part of an ACC that a slice boundary splits,
+   and keeps every XCD's ACCs: a split ACC's (row block, head) units are laid
+   out in folded order (longest, shortest, second longest, ...) before the
+   slices cut it, so under a causal mask each XCD's share of the work is
+   within one row block of the mean; and on such an XCD a piece runs merged
+   with the adjacent whole ACC, longest row block first, so the XCD's
+   longest workgroups do not start last. */
 #define ATTN_MAP_BALANCED_SPLIT 8
 
 /*

@@ -49,18 +49,27 @@ m reversed).
 Added (not on the pages): BALANCED_SPLIT, the fallback made work-balanced
 for causal attention (the digest's §7 implementation notes leave the
 fallback open; the commentary page raises H_Q = 12 over 8 XCDs without a
-remedy).  It changes Swizzled Head-first only (other modes ignore it).  The
-balanced slices stay as they are, so every XCD still takes its ACCs in one
-contiguous run; but an ACC that a slice boundary splits takes its
-(row block, head) units in folded order: the longest-first list with its
-first unit, then its last, then its second, then its second-to-last, ...
-Under a causal mask row block m carries work that grows linearly with m, so
-each consecutive pair of the folded list carries the same work, and the
-pieces of a split ACC on two XCDs carry work in proportion to their unit
-counts.  Pinned by properties (bijection; identical to the mode without the
-bit wherever no ACC is split and for every other base mode; the ACC-per-XCD
-structure unchanged; per-XCD causal work within one row block's work of the
-mean, where the plain slices are off by up to 16% at H_Q = 12).
+remedy).  It changes Swizzled Head-first only (other modes ignore it), and
+only on XCDs whose slice holds part of an ACC that a slice boundary splits.
+The slices stay as they are, so every XCD keeps the same ACCs; two things
+change:
+* which units of a split ACC each XCD gets: the ACC's (row block, head)
+  units are laid out in folded order (its longest-first list taken first,
+  last, second, second-to-last, ...) before the slices cut it, so under a
+  causal mask, where row block m carries work linear in m, each XCD's piece
+  carries work in proportion to its unit count;
+* the order in which such an XCD runs its units: a piece is merged with the
+  adjacent whole ACC of the slice (a leading piece with the first whole ACC,
+  a trailing piece with the last; with fewer than two whole ACCs everything
+  in the slice is one group) and each merged group runs longest first
+  (row block descending, then ACC, then head), the list-scheduling order
+  that keeps the XCD's longest workgroups from starting last.  Groups run in
+  slice order; a group of one whole ACC keeps the order of the other bits.
+Pinned by properties (bijection; identical to the mode without the bit on
+every XCD without a piece and for every other base mode; each XCD keeps its
+ACCs; per-XCD causal work within one row block's work of the mean, where the
+plain slices are off by up to 16% at H_Q = 12; merged groups non-increasing
+in row block).
 
 Parity status: pinned.  On the domain where the pages print formulas (one
 batch, X dividing H_Q, X dividing W) tests/test_remap_oracle.py checks
@@ -151,12 +160,53 @@ def folded(units):
     return out
 
 
-@functools.lru_cache(maxsize=64)
-def _folded_units(M: int, G: int):
-    """(row block, head within the KV group) of an ACC's units: the
-    longest-first list (row block M-1 .. 0, a row block's G heads adjacent)
-    in folded order."""
-    return tuple(folded([(M - 1 - md, hg) for md in range(M) for hg in range(G)]))
+@functools.lru_cache(maxsize=16)
+def _balanced_table(B: int, H_Q: int, M: int, X: int, G: int, longest_first: bool):
+    """(b, h, m) of every workgroup id under SHF + BALANCED_SPLIT, built by
+    listing: the ACC-major order with split ACCs folded, cut into the XCD
+    slices, each slice's ACC parts grouped and the groups with a piece sorted
+    longest first, the k-th unit of XCD x going to id x + k X."""
+    H_KV = H_Q // G
+    U = G * M
+    W = B * H_Q * M
+    starts = slice_starts(W, X)
+    seq = []
+    for a in range(B * H_KV):
+        b, kv = divmod(a, H_KV)
+        if longest_first:
+            units = [(M - 1 - md, kv * G + hg) for md in range(M) for hg in range(G)]
+        else:
+            units = [(m, kv * G + hg) for hg in range(G) for m in range(M)]
+        if acc_is_split(a, G, M, W, X):
+            units = folded([(M - 1 - md, kv * G + hg) for md in range(M) for hg in range(G)])
+        seq += [(a, b, h, m) for m, h in units]
+    table = [None] * W
+    for x in range(X):
+        part_list = []                       # runs of one ACC inside the slice
+        for item in seq[starts[x]:starts[x + 1]]:
+            if part_list and part_list[-1][0][0] == item[0]:
+                part_list[-1].append(item)
+            else:
+                part_list.append([item])
+        whole = [i for i, p in enumerate(part_list) if len(p) == U]
+        has_piece = len(whole) < len(part_list)
+        if not has_piece:
+            groups = [[i] for i in range(len(part_list))]
+        elif len(whole) <= 1:
+            groups = [list(range(len(part_list)))]
+        else:
+            first, last = whole[0], whole[-1]
+            groups = ([list(range(0, first + 1))] + [[i] for i in range(first + 1, last)]
+                      + [list(range(last, len(part_list)))])
+        order = []
+        for g in groups:
+            items = [it for i in g for it in part_list[i]]
+            if any(len(part_list[i]) < U for i in g):
+                items = sorted(items, key=lambda it: (-it[3], it[0], it[2]))
+            order += items
+        for k, (_, b, h, m) in enumerate(order):
+            table[x + k * X] = (b, h, m)
+    return tuple(table)
 
 
 def wg_map(mode: int, w: int, B: int, H_Q: int, N: int, X: int,
@@ -174,11 +224,7 @@ def wg_map(mode: int, w: int, B: int, H_Q: int, N: int, X: int,
     L = chiplet_swizzle(w, W, X) if base in (SBF, SHF) else w
     head_first = base in (NHF, SHF)
     if base == SHF and mode & BALANCED_SPLIT:
-        a, s = divmod(L, G * M)            # global ACC (b, kv) and position in it
-        if acc_is_split(a, G, M, W, X):
-            b, kv = divmod(a, H_Q // G)
-            m, hg = _folded_units(M, G)[s]
-            return b, kv * G + hg, m
+        return _balanced_table(B, H_Q, M, X, G, longest_first)[w]
     if longest_first and head_first:
         b, r = divmod(L, H_Q * M)
         acc, s = divmod(r, G * M)

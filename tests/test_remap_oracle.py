@@ -325,29 +325,36 @@ def test_balanced_split_is_a_bijection_in_every_mode():
             assert len(set(tab)) == len(tab) == oracle.num_workgroups(B, H_Q, N, bm), mode
 
 
-def test_balanced_split_changes_only_the_split_accs_of_shf():
-    """Other base modes ignore the bit; under SHF a workgroup of an ACC that
-    no slice boundary splits computes what it computes without the bit."""
+def _xcd_has_piece(B, H_Q, H_KV, N, X, bm, x):
+    """Whether XCD x's slice holds part of an ACC that a slice boundary splits."""
+    G = H_Q // H_KV
+    M = oracle.row_blocks(N, bm)
+    U = G * M
+    W = B * H_Q * M
+    starts = oracle.slice_starts(W, X)
+    lo, hi = starts[x], starts[x + 1]
+    return any(oracle.acc_is_split(a, G, M, W, X) for a in range(lo // U, (hi - 1) // U + 1)) if hi > lo else False
+
+
+def test_balanced_split_changes_only_xcds_holding_a_split_piece():
+    """Other base modes ignore the bit; under SHF every XCD whose slice holds
+    no piece of a split ACC runs exactly what it runs without the bit."""
     for B, H_Q, H_KV, N, X, bm in _bal_shapes(80, seed=12):
         G = H_Q // H_KV
-        M = oracle.row_blocks(N, bm)
-        W = B * H_Q * M
         for base in (0, 1, 2, 4, 5, 6):
             assert (oracle.wg_table(base | BAL, B, H_Q, N, X, bm, G)
                     == oracle.wg_table(base, B, H_Q, N, X, bm, G))
         for lf in (0, oracle.LONGEST_FIRST):
             plain = oracle.wg_table(SHF | lf, B, H_Q, N, X, bm, G)
             bal = oracle.wg_table(SHF | lf | BAL, B, H_Q, N, X, bm, G)
-            for w in range(W):
-                a = oracle.chiplet_swizzle(w, W, X) // (G * M)
-                if not oracle.acc_is_split(a, G, M, W, X):
+            for w in range(len(plain)):
+                if not _xcd_has_piece(B, H_Q, H_KV, N, X, bm, w % X):
                     assert bal[w] == plain[w]
 
 
 def test_balanced_split_keeps_each_acc_on_its_xcds():
-    """The XCDs of every ACC are those of plain SHF (each XCD's ACCs one
-    contiguous run; an ACC on at most 2 XCDs when there are at least X ACCs),
-    and a split ACC's piece on each XCD has the unit count it had."""
+    """Every XCD keeps the ACCs (and unit counts per ACC) it has under plain
+    SHF; an ACC spans at most 2 XCDs when there are at least X ACCs."""
     for B, H_Q, H_KV, N, X, bm in _bal_shapes(80, seed=13):
         G = H_Q // H_KV
         per_plain, per_bal = defaultdict(list), defaultdict(list)
@@ -357,14 +364,65 @@ def test_balanced_split_keeps_each_acc_on_its_xcds():
             per_plain[w % X].append(_acc(b, h, H_Q, H_KV))
             per_bal[w % X].append(_acc(b2, h2, H_Q, H_KV))
         for x in per_plain:
-            assert per_bal[x] == per_plain[x]
-            assert per_bal[x] == sorted(per_bal[x])
+            assert sorted(per_bal[x]) == sorted(per_plain[x])
         if B * H_KV >= X:
             spans = defaultdict(set)
             for x, accs in per_bal.items():
                 for a in accs:
                     spans[a].add(x)
             assert all(len(s) <= 2 for s in spans.values())
+
+
+def test_balanced_split_runs_merged_groups_longest_first():
+    """On an XCD that holds a piece, the units run in non-increasing row
+    block within each merged group, and at most two ACCs are interleaved at
+    any point (a piece only merges with its neighbouring whole ACC)."""
+    for B, H_Q, H_KV, N, X, bm in _bal_shapes(80, seed=15):
+        G = H_Q // H_KV
+        M = oracle.row_blocks(N, bm)
+        tab = oracle.wg_table(SHF | 4 | BAL, B, H_Q, N, X, bm, G)
+        for x in range(X):
+            if not _xcd_has_piece(B, H_Q, H_KV, N, X, bm, x):
+                continue
+            seq = [tab[w] for w in range(x, len(tab), X)]
+            accs = sorted({_acc(b, h, H_Q, H_KV) for b, h, _ in seq})
+            # count how many ACCs have started but not finished at each point
+            first = {a: min(i for i, (b, h, _) in enumerate(seq) if _acc(b, h, H_Q, H_KV) == a) for a in accs}
+            last = {a: max(i for i, (b, h, _) in enumerate(seq) if _acc(b, h, H_Q, H_KV) == a) for a in accs}
+            whole = sum(1 for a in accs if sum(1 for b, h, _ in seq if _acc(b, h, H_Q, H_KV) == a) == G * M)
+            live = max(sum(1 for a in accs if first[a] <= i <= last[a]) for i in range(len(seq)))
+            assert live <= (3 if whole <= 1 else 2), (B, H_Q, H_KV, N, X, x)
+            # longest first inside every run where ACCs interleave
+            for i in range(1, len(seq)):
+                a0, a1 = _acc(*seq[i - 1][:2], H_Q, H_KV), _acc(*seq[i][:2], H_Q, H_KV)
+                together = first[a1] < last[a0] and first[a0] < last[a1]
+                if together:
+                    assert seq[i][2] <= seq[i - 1][2], (x, i)
+
+
+def test_balanced_split_c4_prime_makespan():
+    """B=1, H=12, N=32K, 256-row blocks, 8 XCDs of 32 CUs: list scheduling
+    of each XCD's workgroups in dispatch order (lengths = visible key tiles)
+    finishes within 5% of the ideal (the XCD's work over its CUs) with the
+    balanced split; longest first alone leaves 16.5% (the heavy half of a
+    split ACC on one XCD)."""
+    import heapq
+    N, bm = 32768, 256
+
+    def makespan(mode):
+        tab = oracle.wg_table(mode, 1, 12, N, 8, bm, 1)
+        worst, total = 0, 0
+        for x in range(8):
+            lengths = [min(N, (m + 1) * bm) // 32 for (_, _, m) in tab[x::8]]
+            total += sum(lengths)
+            cus = [0] * 32
+            for ln in lengths:
+                t = heapq.heappop(cus)
+                heapq.heappush(cus, t + ln)
+            worst = max(worst, max(cus))
+        return worst / (total / 8 / 32)
+    assert round(makespan(SHF | 4), 3) == 1.165
+    assert makespan(SHF | 4 | BAL) <= 1.05
 
 
 def test_balanced_split_per_xcd_causal_work_within_a_row_block_of_the_mean():
