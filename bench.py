@@ -694,7 +694,7 @@ def run_bwd(args, attn, inputs):
     dout = inputs.normal_bf16((B, H_Q, N, d), 1003, "cuda")
     o, lse = attn.attn_fwd(q, k, v, causal=causal)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty((2, B, H_Q, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty((B, H_Q, 2, N), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     results = {}
     for mode in modes:

@@ -370,7 +370,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              stream: torch.cuda.Stream | None = None):
     """Gradients (dq, dk, dv) of sum(dout * o) for o, lse = attn_fwd(q, k, v,
     causal).  q, o, dout [B,H_Q,N,d] and k, v [B,H_KV,N,d] contiguous bf16;
-    lse fp32 [B,H_Q,N].  Outputs and the fp32 workspace ws [2,B,H_Q,N] are
+    lse fp32 [B,H_Q,N].  Outputs and the fp32 workspace ws [B,H_Q,2,N] are
     allocated when not given.  Enqueued on ``stream``; returns without
     synchronising."""
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
@@ -389,8 +389,8 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         _check_out(name, t, ref.shape, torch.bfloat16, q.device)
     if ws is None:
-        ws = torch.empty((2, B, H_Q, N), dtype=torch.float32, device=q.device)
-    _check_out("ws", ws, (2, B, H_Q, N), torch.float32, q.device)
+        ws = torch.empty((B, H_Q, 2, N), dtype=torch.float32, device=q.device)
+    _check_out("ws", ws, (B, H_Q, 2, N), torch.float32, q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),

@@ -23,20 +23,13 @@ struct BwdArgs {
   float scale_log2, scale;
 };
 
-// 32-key blocks per wave of the dK/dV kernel (the workgroup covers
-// 128 * kKeyBlocks keys).  One block keeps two waves per SIMD.  Two blocks
-// halve the LDS reads per MFMA but need one wave per SIMD (their
-// accumulators fill the register file), and measured slower at both head
-// dims (d=64: 487 against 625 TFLOP/s; d=128 spills).
-constexpr int kKeyBlocks = 1;
-
 template <int D, bool CAUSAL, bool FULL_D>
 hipError_t launch_bwd_one(const BwdArgs& a, hipStream_t s) {
   const auto* q = static_cast<const uint16_t*>(a.q);
   const auto* k = static_cast<const uint16_t*>(a.k);
   const auto* v = static_cast<const uint16_t*>(a.v);
   const auto* dout = static_cast<const uint16_t*>(a.dout);
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, CAUSAL, FULL_D, kKeyBlocks>),
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, CAUSAL, FULL_D>),
                      dim3(a.B * a.H_KV * a.M_kv), dim3(kBwdThreads), 0, s, q, k, v, dout, a.ws,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.B, a.H_Q,
                      a.H_KV, a.N, a.d, a.M_kv, a.mapping, a.X, a.scale_log2, a.scale);
@@ -88,12 +81,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), lse,
-                     ws, rows, d);
+                     ws, rows, d, N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "attn_bwd preprocess launch");
   const double scale = 1.0 / std::sqrt((double)d);
-  const int M_kv = (int)(((int64_t)N + kBwdBlock * kKeyBlocks - 1) / (kBwdBlock * kKeyBlocks));
-  BwdArgs a{q, k, v, dout, ws, dq, dk, dv, B, H_Q, H_KV, N, d, M_kv, (int)M_b, mapping, X,
+  const int M_kv = (int)M_b;
+  BwdArgs a{q, k, v, dout, ws, dq, dk, dv, B, H_Q, H_KV, N, d, M_kv, M_kv, mapping, X,
             (float)(1.4426950408889634 * scale), (float)scale};
   e = (d <= 64) ? launch_bwd<64>(a, causal, s) : launch_bwd<128>(a, causal, s);
   if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");

@@ -44,10 +44,11 @@ constexpr int kBwdThreads = 256;
 constexpr int kBwdTile = 32;     // rows of a streamed tile
 
 // D = rowsum(dO * O) (fp32) and lse * log2(e), one wave per row; lane l owns
-// columns 2l, 2l+1.  ws holds [lse2 | D], each rows floats.
+// columns 2l, 2l+1.  ws holds [lse2 | D] of each (batch, query head), N
+// floats each.
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, float* __restrict__ ws, uint64_t rows, int d) {
+    const float* __restrict__ lse, float* __restrict__ ws, uint64_t rows, int d, int N) {
   const int lane = threadIdx.x & 63;
   const uint64_t row = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -62,8 +63,9 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(
 #pragma unroll
   for (int s = 32; s > 0; s >>= 1) acc += __shfl_xor(acc, s, 64);
   if (lane == 0) {
-    ws[row] = lse[row] * 1.4426950408889634f;
-    ws[rows + row] = acc;
+    const uint64_t head = row / (uint64_t)N, r = row - head * (uint64_t)N;
+    ws[head * 2u * N + r] = lse[row] * 1.4426950408889634f;
+    ws[head * 2u * N + N + r] = acc;
   }
 }
 
@@ -178,26 +180,69 @@ __device__ __forceinline__ void bwd_load_tile(u32x4 desc, int row0, int head_row
   }
 }
 
-// KB key blocks of 32 per wave (KB * 128 keys per workgroup).  With KB = 2
-// every Q and dO fragment read from LDS feeds two MFMAs (half the LDS traffic
-// per MFMA); the 2 x 128 dK/dV accumulators then need one wave per SIMD.
-template <int D, bool CAUSAL, bool FULL_D, int KB>
-__global__ __launch_bounds__(kBwdThreads, KB == 1 ? 2 : 1) void attn_bwd_dkv_kernel(
+// ---------------------------------------------------------------------------
+// dK/dV kernel.  One workgroup per (batch, KV head, 128-key block): four waves
+// of 32 keys, one wave per SIMD.  K^T and V^T of a wave's keys (the B
+// operands of S = Q K^T and dP = dO V^T) and the dK^T, dV^T accumulators sit
+// in AGPRs for the whole kernel.  The workgroup streams 32-row tiles of Q and
+// dO, of every query head of the KV group, through a ring of kDkvStages LDS
+// stages; a tile is loaded LDS-direct three tiles before its first use,
+// together with its rows' lse2 and D (one 256-byte copy per wave).
+//
+// The body of tile t is one static schedule of MFMA "bundles":
+//   first part:  dV^T += dO^T P and dK^T += Q^T dS of tile t-1, while the
+//                VALU forms P and dS of tile t from its S and dP;
+//   second part: S and dP of tile t+1;
+//   tail:        the first operand fragments of the next body and the stats
+//                of tile t+1 are read, then one barrier.
+// Every LDS operand is read AHEAD bundles before its MFMA, so after the
+// barrier the next body starts with its operands in registers.  The ring
+// needs five stages: in body t the MFMAs read tiles t-1 and t+1 and the
+// stats of tile t, and the loads go to tile t+3.
+constexpr int kDkvStages = 5;
+
+template <int D>
+struct DkvCfg {
+  using C = BwdCfg<D>;
+  static constexpr int DO0 = kDkvStages * C::TILE_B;      // dO tiles (Q tiles at 0)
+  static constexpr int ST0 = 2 * kDkvStages * C::TILE_B;  // stats of stage s, wave w
+  static constexpr int ST_STAGE = 4 * 256;
+  static constexpr int BYTES = ST0 + kDkvStages * ST_STAGE;
+  static constexpr int LPT = 2 * C::SLOTS + 1;  // LDS-direct loads per thread and tile
+  static constexpr int NA = 4 * C::DB;          // dV and dK MFMAs of a tile
+  static constexpr int NB = 2 * C::KC;          // S and dP MFMAs of a tile
+  static constexpr int NF = NA + NB;            // bundles per tile
+  static constexpr int AHEAD = 4;               // operand fragments in flight
+  // Bundles over which P and dS of a tile are formed: the first part when it
+  // has 16 MFMAs (D = 128), else the whole tile.
+  static constexpr int NV = NA >= 16 ? NA : NF;
+  static_assert(BYTES <= 160 * 1024, "LDS");
+  static_assert(kDkvStages * C::TILE_B <= 65536 - C::TILE_B, "stage offsets fit ds_read immediates");
+};
+
+// LDS-direct load of 4 bytes per lane: lane l writes LDS at M0 + 4 l.
+__device__ __forceinline__ void load_lds_dword(u32x4 desc, uint32_t voff, uint32_t m0) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(desc), "s"(m0)
+      : "memory", "m0");
+}
+
+template <int D, bool CAUSAL, bool FULL_D>
+__global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ ws, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
     int B, int H_Q, int H_KV, int N, int d, int M, int mapping, int num_xcd,
     float scale_log2, float scale) {
   using C = BwdCfg<D>;
-  // LDS: 2 x (Q tile, dO tile), then 2 x [lse2 of the tile's 32 rows | D].
-  constexpr int kStat = 4 * C::TILE_B;
-  constexpr int kLdsB = kStat + 2 * 64 * 4;
-  __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsB / 4];
+  using L = DkvCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[L::BYTES / 4];
   char* const lb = reinterpret_cast<char*>(lds);
-  float* const stat = reinterpret_cast<float*>(lb + kStat);
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lb);
-  auto q_tile = [&](int buf) { return buf * 2 * C::TILE_B; };
-  auto do_tile = [&](int buf) { return buf * 2 * C::TILE_B + C::TILE_B; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int g = lane >> 5, l32 = lane & 31;
@@ -207,199 +252,357 @@ __global__ __launch_bounds__(kBwdThreads, KB == 1 ? 2 : 1) void attn_bwd_dkv_ker
   // the least work under a causal mask, and for keys that is the last block
   // (it is seen by the fewest query rows).
   const WgCoord wc = wg_map_uniform(mapping, blockIdx.x, B, H_KV, M, num_xcd, 1);
-  const int key0 = (M - 1 - (int)wc.m) * kBwdBlock * KB;
-  int my_key[KB];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) my_key[kb] = key0 + (wave * KB + kb) * 32 + l32;
+  const int key0 = (M - 1 - (int)wc.m) * kBwdBlock;
+  const int my_key = key0 + wave * 32 + l32;
   const int dd = FULL_D ? D : d;
   const uint32_t head_elems = (uint32_t)N * (uint32_t)dd;
+  const uint32_t head_bytes = head_elems * 2u;
   const uint64_t kv_head = ((uint64_t)wc.b * H_KV + wc.h) * head_elems;
-  const uint64_t rows = (uint64_t)B * H_Q * N;
-  const TileAddr<D> ta(lane);
 
-  // K and V of this lane's keys, B operands (K^T, V^T): dims 16kc + 8g .. +7.
-  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + kv_head, head_elems * 2);
-  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v + kv_head, head_elems * 2);
-  bf16x8 kf[KB][C::KC], vf[KB][C::KC];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc) {
-      const int col = kc * 16 + g * 8;
-      const uint32_t off =
-          (FULL_D || col < dd) ? (uint32_t)(my_key[kb] * dd + col) * 2u : kOutOfRange;
-      kf[kb][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(k_rs, off, 0, 0));
-      vf[kb][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(v_rs, off, 0, 0));
-    }
+  // K^T and V^T of this lane's key (B operands): dims 16kc + 8g .. +7.
+  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + kv_head, head_bytes);
+  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v + kv_head, head_bytes);
+  bf16x8 kf[C::KC], vf[C::KC];
+  static_for<C::KC>([&](auto kci) {
+    constexpr int kc = decltype(kci)::value;
+    const int col = kc * 16 + g * 8;
+    const uint32_t off = (FULL_D || col < dd) ? (uint32_t)(my_key * dd + col) * 2u : kOutOfRange;
+    kf[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(k_rs, off, 0, 0));
+    vf[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(v_rs, off, 0, 0));
+  });
+  static_for<C::KC>([&](auto kci) {
+    xdl_guard_a(kf[decltype(kci)::value]);
+    xdl_guard_a(vf[decltype(kci)::value]);
+  });
 
-  // Padded head-dim columns are never written by the tile loads.
-  if (!FULL_D) {
-    for (int i = tid; i < kStat / 16; i += kBwdThreads)
-      *reinterpret_cast<u32x4*>(lb + i * 16) = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-  }
-
-  // Query tiles: every head of the group, tiles qt0 .. nq-1 of each (causal:
-  // rows before the block see none of its keys).
-  const int nq = (N + kBwdTile - 1) / kBwdTile;
-  const int qt0 = CAUSAL ? key0 / kBwdTile : 0;
-  const int per_head = nq - qt0;
-  const int n_iter = G * per_head;
-  auto issue = [&](int it, int buf) {
-    const int hg = it / per_head, qt = qt0 + (it - hg * per_head);
-    const uint64_t q_head = ((uint64_t)wc.b * H_Q + (int)wc.h * G + hg) * head_elems;
-    bwd_load_tile<D, FULL_D>(make_desc(q + q_head, head_elems * 2), qt * kBwdTile, N, dd,
-                             lds_base, q_tile(buf), tid);
-    bwd_load_tile<D, FULL_D>(make_desc(dout + q_head, head_elems * 2), qt * kBwdTile, N, dd,
-                             lds_base, do_tile(buf), tid);
-  };
-  // lse2 and D of a tile's rows reach LDS through the registers of wave 0.
-  float st_l = 0.f, st_d = 0.f;
-  auto stat_load = [&](int it) {
-    const int hg = it / per_head, qt = qt0 + (it - hg * per_head);
-    const int r = min(qt * kBwdTile + l32, N - 1);
-    const uint64_t idx = ((uint64_t)wc.b * H_Q + (int)wc.h * G + hg) * N + r;
-    st_l = ws[idx];
-    st_d = ws[rows + idx];
-  };
-  auto stat_store = [&](int buf) {
-    if (tid < 32) {
-      stat[buf * 64 + tid] = st_l;
-      stat[buf * 64 + 32 + tid] = st_d;
-    }
-  };
-
-  f32x16 dk_acc[KB][C::DB], dv_acc[KB][C::DB];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      dk_acc[kb][db] = f32x16{};
-      dv_acc[kb][db] = f32x16{};
-    }
-  if (n_iter > 0) {
-    issue(0, 0);
-    if (wave == 0) stat_load(0);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  stat_store(0);
+  // Zeroed LDS: the stage of "tile -1" that the first body multiplies by
+  // P = dS = 0, and the padded head-dim columns.
+  for (int i = tid; i < L::BYTES / 16; i += kBwdThreads)
+    *reinterpret_cast<u32x4*>(lb + i * 16) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
-  for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
-    const int qt = qt0 + it % per_head;
-    if (it + 1 < n_iter) {
-      issue(it + 1, buf ^ 1);
-      if (wave == 0) stat_load(it + 1);
-    }
-    // S = Q K^T and dP = dO V^T for this wave's keys: lane (key l32 of block
-    // kb, half g) holds rows 8(r/4) + 4g + (r%4) of the tile.  Each LDS
-    // fragment feeds the KB key blocks.
-    f32x16 s[KB], dp[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
-    }
-#pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc) {
-      const bf16x8 qa = lds_row_frag<D>(lb, q_tile(buf), ta, kc);
-      const bf16x8 da = lds_row_frag<D>(lb, do_tile(buf), ta, kc);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kb][kc], s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kb][kc], dp[kb], 0, 0, 0);
-      }
-    }
-    const float* st = stat + buf * 64;
-    uint32_t pk[KB][8], dsk[KB][8];
-    // P and dS of the tile, rounded to bf16; MASKED adds the per-element test
-    // (a row past N, a key past N, causal: a key after the row).
-    auto softmax_grad = [&](auto masked) {
-      constexpr bool MASKED = decltype(masked)::value;
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const f32x4 lrow = *reinterpret_cast<const f32x4*>(st + 8 * c4 + 4 * g);
-        const f32x4 drow = *reinterpret_cast<const f32x4*>(st + 32 + 8 * c4 + 4 * g);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          float p4[4], ds4[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * c4 + e;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, -lrow[e]));
-            if constexpr (MASKED) {
-              const int qrow = qt * kBwdTile + 8 * c4 + 4 * g + e;
-              const bool ok = qrow < N && my_key[kb] < N && (!CAUSAL || my_key[kb] <= qrow);
-              p = ok ? p : 0.f;
-            }
-            p4[e] = p;
-            ds4[e] = p * (dp[kb][r] - drow[e]);
-          }
-          pk[kb][2 * c4] = pack_bf16x2(p4[0], p4[1]);
-          pk[kb][2 * c4 + 1] = pack_bf16x2(p4[2], p4[3]);
-          dsk[kb][2 * c4] = pack_bf16x2(ds4[0], ds4[1]);
-          dsk[kb][2 * c4 + 1] = pack_bf16x2(ds4[2], ds4[3]);
-        }
-      }
-    };
-    // The test is needed only where some (row, key) pair of the wave is out:
-    // the tile holding row N-1, the key block holding key N-1, and (causal)
-    // tiles whose first row is before the wave's last key.
-    const int wave_key_end = key0 + (wave + 1) * KB * 32;  // one past the wave's keys
-    const bool full = (qt + 1) * kBwdTile <= N && wave_key_end <= N &&
-                      (!CAUSAL || qt * kBwdTile >= wave_key_end - 1);
-    if (full)
-      softmax_grad(std::false_type{});
+  // ---- Tile sequence: every query head hg of the group, row tiles qt0 ..
+  // nq-1 of each (causal: rows before the block see none of its keys).
+  const int nq = (N + kBwdTile - 1) / kBwdTile;
+  const int qt0 = CAUSAL ? key0 / kBwdTile : 0;
+  const int n_iter = G * (nq - qt0);
+  const uint64_t q_head0 = ((uint64_t)wc.b * H_Q + (uint64_t)wc.h * G) * head_elems;
+  const uint64_t st_head0 = ((uint64_t)wc.b * H_Q + (uint64_t)wc.h * G) * 2u * (uint64_t)N;
+
+  // LDS-direct slots of this thread in a tile: slot P = tid + 256 i holds
+  // row P / CPR, chunk (P % CPR) ^ swz(row).
+  uint32_t slot_off[C::SLOTS];
+  static_for<C::SLOTS>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    const int P = tid + kBwdThreads * i;
+    const int row = P / C::CPR;
+    const int chunk = (P % C::CPR) ^ C::swz(row);
+    slot_off[i] = (FULL_D || chunk * 8 < dd) ? (uint32_t)(row * dd + chunk * 8) * 2u : kOutOfRange;
+  });
+  // The loads of tile (hg, qt) into stage `stage`: descriptors and offsets
+  // (a tile past the sequence, hg == G, reads nothing and writes zeros),
+  // issued one instruction per bundle by issue_one<i>, i < LPT.
+  struct LoadPlan {
+    u32x4 q_desc, do_desc, st_desc;
+    uint32_t soff, st_voff, stage_off;
+  };
+  auto plan = [&](int hg, int qt, int stage) {
+    LoadPlan lp;
+    const bool valid = hg < G;
+    const int hh = valid ? hg : 0;
+    const uint64_t qo = q_head0 + (uint64_t)hh * head_elems;
+    lp.q_desc = make_desc(q + qo, head_bytes);
+    lp.do_desc = make_desc(dout + qo, head_bytes);
+    const uint32_t soff0 = (uint32_t)(qt * kBwdTile) * (uint32_t)dd * 2u;
+    lp.soff = (valid && soff0 < head_bytes) ? soff0 : head_bytes;
+    // Stats: lanes 0-31 lse2 of rows qt*32 + l32, lanes 32-63 their D.
+    lp.st_desc = make_desc(ws + st_head0 + (uint64_t)hh * 2u * (uint64_t)N, (uint32_t)N * 8u);
+    const int r = min(qt * kBwdTile + l32, N - 1);
+    lp.st_voff = valid ? (uint32_t)(g * N + r) * 4u : kOutOfRange;
+    lp.stage_off = (uint32_t)stage;
+    return lp;
+  };
+  auto issue_one = [&](const LoadPlan& lp, auto ii) {
+    constexpr int i = decltype(ii)::value;
+    const uint32_t stage = lp.stage_off;
+    if constexpr (i < C::SLOTS)
+      load_lds(lp.q_desc, slot_off[i], lp.soff,
+               lds_base + stage * C::TILE_B + (wave + 4 * i) * 1024);
+    else if constexpr (i < 2 * C::SLOTS)
+      load_lds(lp.do_desc, slot_off[i - C::SLOTS], lp.soff,
+               lds_base + L::DO0 + stage * C::TILE_B + (wave + 4 * (i - C::SLOTS)) * 1024);
     else
-      softmax_grad(std::true_type{});
-    // dV^T += dO^T P and dK^T += Q^T dS, k = the tile's rows (16 per chunk c);
-    // each transposed fragment feeds the KB key blocks.
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const bf16x8 dot = lds_tr_frag<D>(lb, do_tile(buf), ta, c, db);
-        const bf16x8 qt_ = lds_tr_frag<D>(lb, q_tile(buf), ta, c, db);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8 pb = __builtin_bit_cast(
-              bf16x8, u32x4{pk[kb][4 * c], pk[kb][4 * c + 1], pk[kb][4 * c + 2], pk[kb][4 * c + 3]});
-          const bf16x8 sb = __builtin_bit_cast(
-              bf16x8, u32x4{dsk[kb][4 * c], dsk[kb][4 * c + 1], dsk[kb][4 * c + 2], dsk[kb][4 * c + 3]});
-          dv_acc[kb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, pb, dv_acc[kb][db], 0, 0, 0);
-          dk_acc[kb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt_, sb, dk_acc[kb][db], 0, 0, 0);
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    if (it + 1 < n_iter) stat_store(buf ^ 1);
-    __syncthreads();
+      load_lds_dword(lp.st_desc, lp.st_voff,
+                     lds_base + L::ST0 + stage * L::ST_STAGE + wave * 256);
+  };
+  auto issue = [&](int hg, int qt, int stage) {
+    const LoadPlan lp = plan(hg, qt, stage);
+    static_for<L::LPT>([&](auto ii) { issue_one(lp, ii); });
+  };
+
+  // ---- Per-lane LDS addresses.  Row fragment kc (A operand of S or dP):
+  // row l32, chunk 2kc + g.  Transposed fragment (c, db) (A operand of dV^T
+  // or dK^T): rows 16c + 4g + {0..3} and 16c + 8 + 4g + {0..3} of dims
+  // 32db + ..., two ds_read_b64_tr_b16 8 rows apart (as in lds_tr_frag).
+  int row_q[C::KC], row_do[C::KC], tr_q[C::DB][2], tr_do[C::DB][2];
+  static_for<C::KC>([&](auto kci) {
+    constexpr int kc = decltype(kci)::value;
+    row_q[kc] = l32 * C::ROWB + (((kc * 2 + g) ^ C::swz(l32)) * 16);
+    row_do[kc] = row_q[kc] + L::DO0;
+    pin(row_do[kc]);
+  });
+  {
+    const int j = lane & 15, kk = j >> 2, qq = j & 3, dhalf = (lane >> 4) & 1;
+    const int krow = 4 * g + kk, w = 2 * dhalf + (qq >> 1);
+    static_for<C::DB>([&](auto dbi) {
+      constexpr int db = decltype(dbi)::value;
+      static_for<2>([&](auto hi) {
+        constexpr int h = decltype(hi)::value;
+        tr_q[db][h] = (krow + 8 * h) * C::ROWB +
+                      (((4 * db + w) ^ C::swz(krow + 8 * h)) * 16) + (qq & 1) * 8;
+        tr_do[db][h] = tr_q[db][h] + L::DO0;
+        pin(tr_do[db][h]);
+      });
+    });
   }
+  // The dO and stats regions start above the 16-bit immediate of ds_read:
+  // their base addresses are pinned so that the compiler keeps one register
+  // per address and the stage offsets as immediates.
+  int st_addr = L::ST0 + wave * 256 + 16 * g;
+  pin(st_addr);
+
+  // Operand fragment f of the body whose tile t has stage PH: f < NA the
+  // transposed fragments of tile t-1 (dO^T, Q^T alternating over (c, db)),
+  // then the row fragments of tile t+1 (Q, dO alternating over kc).
+  auto read_frag = [&](auto phi, auto fi) -> bf16x8 {
+    constexpr int PH = decltype(phi)::value, f = decltype(fi)::value;
+    if constexpr (f < L::NA) {
+      constexpr int sp = (PH + kDkvStages - 1) % kDkvStages;
+      constexpr int pair = f / 2, c = pair / C::DB, db = pair % C::DB;
+      constexpr int off = sp * C::TILE_B + c * 16 * C::ROWB;
+      const int a0 = (f % 2 == 0) ? tr_do[db][0] : tr_q[db][0];
+      const int a1 = (f % 2 == 0) ? tr_do[db][1] : tr_q[db][1];
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(lb + off + a0));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(lb + off + a1));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      constexpr int sn = (PH + 1) % kDkvStages;
+      constexpr int kc = (f - L::NA) / 2;
+      const int a = ((f - L::NA) % 2 == 0) ? row_q[kc] : row_do[kc];
+      return *reinterpret_cast<const bf16x8*>(lb + sn * C::TILE_B + a);
+    }
+  };
+  auto read_stats = [&](int stage, f32x4 (&ls)[4], f32x4 (&ds)[4]) {
+    static_for<4>([&](auto ci) {
+      constexpr int c4 = decltype(ci)::value;
+      ls[c4] = *reinterpret_cast<const f32x4*>(lb + st_addr + stage * L::ST_STAGE + 32 * c4);
+      ds[c4] = *reinterpret_cast<const f32x4*>(lb + st_addr + stage * L::ST_STAGE + 128 + 32 * c4);
+    });
+  };
+
+  f32x16 dk_acc[C::DB], dv_acc[C::DB];
+  static_for<C::DB>([&](auto dbi) {
+    dk_acc[decltype(dbi)::value] = f32x16{};
+    dv_acc[decltype(dbi)::value] = f32x16{};
+  });
+
+  // ---- Prologue: tiles 0-2 in flight, tiles 0 and 1 waited for; S and dP
+  // of tile 0; P = dS = 0 for "tile -1" (its stage is zero).
+  int hg_l = 0, qt_l = qt0;  // next tile to load
+  auto advance = [&](int& hg, int& qt) {
+    if (++qt == nq) {
+      qt = qt0;
+      ++hg;
+    }
+  };
+  static_for<3>([&](auto si) {
+    issue(hg_l, qt_l, decltype(si)::value);
+    advance(hg_l, qt_l);
+  });
+  wait_vmcnt<L::LPT>();
+  barrier();
+  f32x16 s_cur, dp_cur;
+  static_for<C::KC>([&](auto kci) {
+    constexpr int kc = decltype(kci)::value;
+    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(lb + row_q[kc]);
+    const bf16x8 da = *reinterpret_cast<const bf16x8*>(lb + row_do[kc]);
+    mfma_scores<(kc > 0)>(s_cur, qa, kf[kc]);
+    mfma_scores<(kc > 0)>(dp_cur, da, vf[kc]);
+  });
+  uint32_t pk[8], dsk[8];
+  static_for<8>([&](auto i) {
+    pk[decltype(i)::value] = 0u;
+    dsk[decltype(i)::value] = 0u;
+  });
+  bf16x8 fr[L::AHEAD];
+  static_for<L::AHEAD>([&](auto fi) {
+    fr[decltype(fi)::value] = read_frag(std::integral_constant<int, 0>{}, fi);
+  });
+  f32x4 lse4[4], dl4[4];
+  read_stats(0, lse4, dl4);
+
+  // Causal / ragged mask of a lane's element (row 8 c4 + 4g + e of the tile):
+  // visible iff lo <= row < hi, lo = the lane's key (causal) and hi = N (0 for
+  // a key past N).
+  const int m_lo = CAUSAL ? my_key : 0;
+  const int m_span = my_key < N ? max(N - m_lo, 0) : 0;
+  const int wave_key_end = key0 + (wave + 1) * 32;
+  int qt_c = qt0;  // row tile of the tile being computed
+
+  auto body = [&](auto phi, bool masked, int span) {
+    constexpr int PH = decltype(phi)::value;
+    constexpr int s_load = (PH + 3) % kDkvStages, s_next = (PH + 1) % kDkvStages;
+    const LoadPlan lp = plan(hg_l, qt_l, s_load);
+    advance(hg_l, qt_l);
+    xdl_guard_v(s_cur, dp_cur);
+    // A masked element gets S = -inf, hence P = 0 and dS = 0.
+    if (masked) {
+      const int m_a = qt_c * kBwdTile + 4 * g - m_lo;  // row - lo of element 0
+      static_for<16>([&](auto ei) {
+        constexpr int e = decltype(ei)::value;
+        const bool ok = (uint32_t)(m_a + 8 * (e / 4) + e % 4) < (uint32_t)span;
+        s_cur[e] = ok ? s_cur[e] : -__builtin_inff();
+      });
+    }
+    bf16x8 frag[L::NF];
+    static_for<L::AHEAD>([&](auto fi) { frag[decltype(fi)::value] = fr[decltype(fi)::value]; });
+    uint32_t pk_n[8], dsk_n[8];
+    float p_e[16], ds_e[16];
+    f32x16 s_nx, dp_nx;
+    static_for<L::NF>([&](auto fi) {
+      constexpr int f = decltype(fi)::value;
+      if constexpr (f < L::NA) {
+        constexpr int pair = f / 2, c = pair / C::DB, db = pair % C::DB;
+        if constexpr (f % 2 == 0) {
+          const bf16x8 pb = __builtin_bit_cast(
+              bf16x8, u32x4{pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]});
+          mfma_out<0>(dv_acc[db], frag[f], pb);
+        } else {
+          const bf16x8 sb = __builtin_bit_cast(
+              bf16x8, u32x4{dsk[4 * c], dsk[4 * c + 1], dsk[4 * c + 2], dsk[4 * c + 3]});
+          mfma_out<0>(dk_acc[db], frag[f], sb);
+        }
+      } else {
+        constexpr int kc = (f - L::NA) / 2;
+        if constexpr ((f - L::NA) % 2 == 0)
+          mfma_scores<(kc > 0)>(s_nx, frag[f], kf[kc]);
+        else
+          mfma_scores<(kc > 0)>(dp_nx, frag[f], vf[kc]);
+      }
+      // The tile loads go out one per bundle, behind the MFMA.
+      if constexpr (f < L::LPT) issue_one(lp, fi);
+      if constexpr (f + L::AHEAD < L::NF)
+        frag[f + L::AHEAD] = read_frag(phi, std::integral_constant<int, f + L::AHEAD>{});
+      // P and dS of the elements scheduled in this bundle.
+      static_for<16>([&](auto ei) {
+        constexpr int e = decltype(ei)::value;
+        if constexpr (e * L::NV / 16 == f) {
+          constexpr int c4 = e / 4, ee = e % 4;
+          // Inputs and results are pinned to this bundle, so that the
+          // arithmetic neither moves ahead of earlier MFMAs nor sinks into
+          // the next body.
+          float sv = s_cur[e], dpv = dp_cur[e];
+          pin(sv);
+          pin(dpv);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, scale_log2, -lse4[c4][ee]));
+          p_e[e] = p;
+          ds_e[e] = p * (dpv - dl4[c4][ee]);
+          if constexpr (e % 2 == 1) {
+            pk_n[e / 2] = pack_bf16x2(p_e[e - 1], p_e[e]);
+            dsk_n[e / 2] = pack_bf16x2(ds_e[e - 1], ds_e[e]);
+            pin(pk_n[e / 2]);
+            pin(dsk_n[e / 2]);
+          }
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // Tail: the next body's first fragments (tile t, stage PH) and the stats
+    // of tile t+1.
+    static_for<L::AHEAD>([&](auto fi) {
+      fr[decltype(fi)::value] = read_frag(std::integral_constant<int, (PH + 1) % kDkvStages>{}, fi);
+    });
+    read_stats(s_next, lse4, dl4);
+    static_for<8>([&](auto i) {
+      pk[decltype(i)::value] = pk_n[decltype(i)::value];
+      dsk[decltype(i)::value] = dsk_n[decltype(i)::value];
+    });
+    s_cur = s_nx;
+    dp_cur = dp_nx;
+    wait_vmcnt<L::LPT>();
+    barrier();
+  };
+  // The tile needs the per-element test only where some (row, key) pair of
+  // the wave is out: the tile holding row N-1, the key block holding key N-1,
+  // and (causal) tiles whose first row is before the wave's last key.  The
+  // sequence is padded to a multiple of the stage count with tiles that are
+  // masked out entirely (their loads write zeros), so the loop has one exit
+  // and the last tile sits in the last stage.
+  const int n_pad = (n_iter + kDkvStages - 1) / kDkvStages * kDkvStages;
+  auto step = [&](auto phi, int t) {
+    const bool pad = t >= n_iter;
+    const bool full = !pad && (qt_c + 1) * kBwdTile <= N && wave_key_end <= N &&
+                      (!CAUSAL || qt_c * kBwdTile >= wave_key_end - 1);
+    body(phi, !full, pad ? 0 : m_span);
+    if (++qt_c == nq) qt_c = qt0;
+  };
+  for (int t = 0; t < n_pad; t += kDkvStages) {
+    step(std::integral_constant<int, 0>{}, t);
+    step(std::integral_constant<int, 1>{}, t + 1);
+    step(std::integral_constant<int, 2>{}, t + 2);
+    step(std::integral_constant<int, 3>{}, t + 3);
+    step(std::integral_constant<int, 4>{}, t + 4);
+  }
+  // dV and dK of the last tile (stage kDkvStages - 1): the first part of one
+  // more body.
+  {
+    bf16x8 frag[L::NA];
+    static_for<L::AHEAD>([&](auto fi) { frag[decltype(fi)::value] = fr[decltype(fi)::value]; });
+    static_for<L::NA>([&](auto fi) {
+      constexpr int f = decltype(fi)::value;
+      constexpr int pair = f / 2, c = pair / C::DB, db = pair % C::DB;
+      if constexpr (f % 2 == 0) {
+        const bf16x8 pb = __builtin_bit_cast(
+            bf16x8, u32x4{pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]});
+        mfma_out<0>(dv_acc[db], frag[f], pb);
+      } else {
+        const bf16x8 sb = __builtin_bit_cast(
+            bf16x8, u32x4{dsk[4 * c], dsk[4 * c + 1], dsk[4 * c + 2], dsk[4 * c + 3]});
+        mfma_out<0>(dk_acc[db], frag[f], sb);
+      }
+      if constexpr (f + L::AHEAD < L::NA)
+        frag[f + L::AHEAD] = read_frag(std::integral_constant<int, 0>{},
+                                       std::integral_constant<int, f + L::AHEAD>{});
+    });
+  }
+  static_for<C::DB>([&](auto dbi) {
+    xdl_guard_a(dk_acc[decltype(dbi)::value]);
+    xdl_guard_a(dv_acc[decltype(dbi)::value]);
+  });
 
   // Accumulator r of block db is dim 32db + 8(r/4) + 4g + (r%4) of the key;
-  // rows past N fall outside the buffer and are dropped.
-  const __amdgpu_buffer_rsrc_t dk_rs = make_rsrc(dk + kv_head, head_elems * 2);
-  const __amdgpu_buffer_rsrc_t dv_rs = make_rsrc(dv + kv_head, head_elems * 2);
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int col = db * 32 + rr * 8 + g * 4;
-        if (FULL_D || col < dd) {
-          const uint32_t off = (uint32_t)(my_key[kb] * dd + col) * 2u;
-          u32x2 w;
-          w.x = pack_bf16x2(dk_acc[kb][db][rr * 4 + 0] * scale, dk_acc[kb][db][rr * 4 + 1] * scale);
-          w.y = pack_bf16x2(dk_acc[kb][db][rr * 4 + 2] * scale, dk_acc[kb][db][rr * 4 + 3] * scale);
-          __builtin_amdgcn_raw_buffer_store_b64(w, dk_rs, off, 0, 0);
-          w.x = pack_bf16x2(dv_acc[kb][db][rr * 4 + 0], dv_acc[kb][db][rr * 4 + 1]);
-          w.y = pack_bf16x2(dv_acc[kb][db][rr * 4 + 2], dv_acc[kb][db][rr * 4 + 3]);
-          __builtin_amdgcn_raw_buffer_store_b64(w, dv_rs, off, 0, 0);
-        }
+  // keys past N fall outside the buffer and are dropped.
+  const __amdgpu_buffer_rsrc_t dk_rs = make_rsrc(dk + kv_head, head_bytes);
+  const __amdgpu_buffer_rsrc_t dv_rs = make_rsrc(dv + kv_head, head_bytes);
+  static_for<C::DB>([&](auto dbi) {
+    constexpr int db = decltype(dbi)::value;
+    static_for<4>([&](auto rri) {
+      constexpr int rr = decltype(rri)::value;
+      const int col = db * 32 + rr * 8 + g * 4;
+      if (FULL_D || col < dd) {
+        const uint32_t off = (uint32_t)(my_key * dd + col) * 2u;
+        u32x2 w;
+        w.x = pack_bf16x2(dk_acc[db][rr * 4 + 0] * scale, dk_acc[db][rr * 4 + 1] * scale);
+        w.y = pack_bf16x2(dk_acc[db][rr * 4 + 2] * scale, dk_acc[db][rr * 4 + 3] * scale);
+        __builtin_amdgcn_raw_buffer_store_b64(w, dk_rs, off, 0, 0);
+        w.x = pack_bf16x2(dv_acc[db][rr * 4 + 0], dv_acc[db][rr * 4 + 1]);
+        w.y = pack_bf16x2(dv_acc[db][rr * 4 + 2], dv_acc[db][rr * 4 + 3]);
+        __builtin_amdgcn_raw_buffer_store_b64(w, dv_rs, off, 0, 0);
       }
-    }
+    });
+  });
 }
 
 template <int D, bool CAUSAL, bool FULL_D>
@@ -428,7 +631,6 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(
   const uint32_t head_elems = (uint32_t)N * (uint32_t)dd;
   const uint64_t q_head = ((uint64_t)wc.b * H_Q + wc.h) * head_elems;
   const uint64_t kv_head = ((uint64_t)wc.b * H_KV + kvh) * head_elems;
-  const uint64_t rows = (uint64_t)B * H_Q * N;
   const TileAddr<D> ta(lane);
 
   // Q and dO of this lane's row as B operands (Q^T, dO^T): dims 16kc+8g..+7.
@@ -442,9 +644,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(
     qf[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(q_rs, off, 0, 0));
     df[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(do_rs, off, 0, 0));
   }
-  const uint64_t ridx = ((uint64_t)wc.b * H_Q + wc.h) * N + (my_row < N ? my_row : N - 1);
+  const uint64_t ridx = ((uint64_t)wc.b * H_Q + wc.h) * 2u * N + (my_row < N ? my_row : N - 1);
   const float lse2 = ws[ridx];
-  const float drow = ws[rows + ridx];
+  const float drow = ws[ridx + N];
 
   // Padded head-dim columns are never written by the tile loads.
   if (!FULL_D) {

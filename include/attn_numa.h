@@ -211,8 +211,9 @@ int attn_merge(const float* o_parts, const float* lse_parts, int num_splits,
  *   lse         device, fp32 [B][H_Q][N], read only: attn_fwd's lse (natural log)
  *   dq          device, bf16 [B][H_Q][N][d], written (every element)
  *   dk, dv      device, bf16 [B][H_KV][N][d], written (every element)
- *   ws          device, fp32 [2][B][H_Q][N], caller-owned workspace:
- *               lse * log2(e), then D; overwritten
+ *   ws          device, fp32 [B][H_Q][2][N], caller-owned workspace: per
+ *               (batch, query head) lse * log2(e) of its rows, then D;
+ *               overwritten
  *   B, H_Q, H_KV, N, d, causal   as attn_fwd (the same mask); also
  *               B*H_Q*ceil(N/128) < 2^31
  *   mapping     ATTN_MAP_* (0..15) as attn_fwd: the dK/dV kernel maps

@@ -71,7 +71,7 @@ def test_backward_writes_every_element():
     dq = torch.full_like(q, float("nan"))
     dk = torch.full_like(k, float("nan"))
     dv = torch.full_like(v, float("nan"))
-    ws = torch.full((2, B, H_Q, N), float("nan"), device="cuda")
+    ws = torch.full((B, H_Q, 2, N), float("nan"), device="cuda")
     attn.attn_bwd(q, k, v, o, dout, lse, causal=True, dq=dq, dk=dk, dv=dv, ws=ws)
     torch.cuda.synchronize()
     for t in (dq, dk, dv):
