@@ -613,8 +613,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(
     int B, int H_Q, int H_KV, int N, int d, int M, int mapping, int num_xcd,
     float scale_log2, float scale) {
   using C = BwdCfg<D>;
-  // LDS: 2 x (K tile, V tile).
-  __shared__ __attribute__((aligned(16))) uint32_t lds[4 * C::TILE_B / 4];
+  // LDS: kDqStages x (K tile, V tile); tile j is loaded three tiles ahead
+  // into stage j % kDqStages.
+  constexpr int kDqStages = 4;
+  constexpr int kLpt = 2 * C::SLOTS;  // LDS-direct loads per thread and tile
+  __shared__ __attribute__((aligned(16))) uint32_t lds[2 * kDqStages * C::TILE_B / 4];
   char* const lb = reinterpret_cast<char*>(lds);
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lb);
   auto k_tile = [&](int buf) { return buf * 2 * C::TILE_B; };
@@ -650,7 +653,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(
 
   // Padded head-dim columns are never written by the tile loads.
   if (!FULL_D) {
-    for (int i = tid; i < 4 * C::TILE_B / 16; i += kBwdThreads)
+    for (int i = tid; i < 2 * kDqStages * C::TILE_B / 16; i += kBwdThreads)
       *reinterpret_cast<u32x4*>(lb + i * 16) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
   }
@@ -658,20 +661,25 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(
   const u32x4 v_desc = make_desc(v + kv_head, head_elems * 2);
   int n_tiles = (N + kBwdTile - 1) / kBwdTile;
   if (CAUSAL) n_tiles = min(n_tiles, (row0 + kBwdBlock + kBwdTile - 1) / kBwdTile);
-  bwd_load_tile<D, FULL_D>(k_desc, 0, N, dd, lds_base, k_tile(0), tid);
-  bwd_load_tile<D, FULL_D>(v_desc, 0, N, dd, lds_base, v_tile(0), tid);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // Tiles past the last write zeros (their rows are out of range), so every
+  // tile issues the same loads and the waits count them uniformly.
+  auto issue = [&](int j) {
+    const int buf = j & (kDqStages - 1);
+    bwd_load_tile<D, FULL_D>(k_desc, j * kBwdTile, N, dd, lds_base, k_tile(buf), tid);
+    bwd_load_tile<D, FULL_D>(v_desc, j * kBwdTile, N, dd, lds_base, v_tile(buf), tid);
+  };
+  issue(0);
+  issue(1);
+  issue(2);
+  wait_vmcnt<2 * kLpt>();
+  barrier();
 
   f32x16 dq_acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) dq_acc[db] = f32x16{};
   for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) {
-      bwd_load_tile<D, FULL_D>(k_desc, (j + 1) * kBwdTile, N, dd, lds_base, k_tile(buf ^ 1), tid);
-      bwd_load_tile<D, FULL_D>(v_desc, (j + 1) * kBwdTile, N, dd, lds_base, v_tile(buf ^ 1), tid);
-    }
+    const int buf = j & (kDqStages - 1);
+    issue(j + 3);  // into the stage of tile j-1, which every wave has finished
     // S^T = K Q^T and dP^T = V dO^T: lane (row l32, half g) holds keys
     // 32j + 8(r/4) + 4g + (r%4).
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -722,8 +730,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(
         dq_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             lds_tr_frag<D>(lb, k_tile(buf), ta, c, db), b_, dq_acc[db], 0, 0, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // Tile j+1 complete (tiles j+2 and j+3 may stay in flight), then the
+    // barrier that also frees tile j's stage.
+    wait_vmcnt<2 * kLpt>();
+    barrier();
   }
   const __amdgpu_buffer_rsrc_t dq_rs = make_rsrc(dq + q_head, head_elems * 2);
 #pragma unroll
