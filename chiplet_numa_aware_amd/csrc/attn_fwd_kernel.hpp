@@ -374,7 +374,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void attn_fwd_kernel(
 
   // ---- Q fragments: B operand of S^T = K Q^T; for query block qb the lane
   // holds Q[row][16kc+8g..+7] of row 64 wave + 32 qb + l32.
-  const int wave_row_first = row0 + wave * 32 * kQB;
+  const int wave_row_first = row0 + wave * 64;
   // Causal positions spanned by the valid rows (< N_rows) of rows [r0, r1]:
   // exact when the rows lie in one unit, else the whole range 0 .. pos_mod-1.
   auto pos_range = [&](int r0, int r1, int& pmin, int& pmax) {
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void attn_fwd_kernel(
   // A wave with no valid row only loads its share of the K/V tiles.
   const bool wave_idle = wave_row_first >= N_rows;
   int wave_pmin = 0, wave_pmax = 0, wg_pmin = 0, wg_pmax = 0;
-  if (!wave_idle) pos_range(wave_row_first, wave_row_first + 32 * kQB - 1, wave_pmin, wave_pmax);
+  if (!wave_idle) pos_range(wave_row_first, wave_row_first + 63, wave_pmin, wave_pmax);
   pos_range(row0, row0 + kBlockM - 1, wg_pmin, wg_pmax);
   int my_row[kQB];
   int my_last_key[kQB];  // causal: last key the row sees
