@@ -7,13 +7,14 @@
 //   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d).
 // Three kernels:
 //   * attn_bwd_pre: per query row, D and lse in log2 units (one wave per row).
-//   * attn_bwd_dkv: one workgroup per (batch, KV head, 128-key block); each
-//     wave owns 32 keys, the block's K and V stay in LDS, and the workgroup
-//     streams 32-row tiles of Q, dO (and the rows' lse, D) of every query
-//     head of the KV group.  dK and dV accumulate in registers: GQA needs no
-//     atomics.
-//   * attn_bwd_dq: one workgroup per (batch, query head, 128-row block); each
-//     wave owns 32 rows (Q and dO in registers) and streams 32-key K/V tiles.
+//   * attn_bwd_dkv: one workgroup per (batch, KV head, 128-key block), one
+//     wave per SIMD; each wave owns 32 keys (K and V in registers) and the
+//     workgroup streams 32-row tiles of Q, dO (and the rows' lse, D) of
+//     every query head of the KV group through a five-stage LDS ring.  dK
+//     and dV accumulate in registers: GQA needs no atomics.
+//   * attn_bwd_dq: one workgroup per (batch, query head, 128-row block), two
+//     per CU; each wave owns 32 rows (Q and dO in registers) and streams
+//     32-key K/V tiles through a four-stage LDS ring.
 // Both gradient kernels take their workgroup coordinates from wg_map, so the
 // four remaps (and longest first) apply as in the forward pass; every output
 // element is written by one workgroup in a fixed order, so results do not
