@@ -6,7 +6,8 @@ import this package.  It shares no code with the HIP path.
 """
 from .sdpa import attention, attention_head_rows, attention_sampled, kv_head
 from .split import causal_offset, merge, partial_attention, partial_head_rows
-from .backward import attention_backward, backward_key_rows, backward_query_rows
+from .backward import (attention_backward, backward_key_rows, backward_query_rows,
+                       backward_zero_keys)
 from .gemm import cac_tile_table, gemm
 from .remap import (NBF, NHF, SBF, SHF, LONGEST_FIRST, BALANCED_SPLIT, MODE_NAMES,
                      acc_is_split, chiplet_swizzle, folded, num_workgroups, row_blocks,
@@ -15,7 +16,7 @@ from .remap import (NBF, NHF, SBF, SHF, LONGEST_FIRST, BALANCED_SPLIT, MODE_NAME
 __all__ = [
     "attention", "attention_head_rows", "attention_sampled", "kv_head",
     "causal_offset", "merge", "partial_attention", "partial_head_rows",
-    "attention_backward", "backward_key_rows", "backward_query_rows",
+    "attention_backward", "backward_key_rows", "backward_query_rows", "backward_zero_keys",
     "cac_tile_table", "gemm",
     "NBF", "NHF", "SBF", "SHF", "LONGEST_FIRST", "BALANCED_SPLIT", "MODE_NAMES",
     "acc_is_split", "chiplet_swizzle", "folded", "num_workgroups", "row_blocks",

@@ -121,3 +121,60 @@ def backward_key_rows(q_heads, k_head, v_head, dout_heads, keys, causal: bool,
             dv += p[:, keys].T @ dout_heads[h, rows]
             dk += (ds[:, keys].T @ q_heads[h, rows]) * scale
     return dk, dv
+
+
+def backward_zero_keys(q_heads, v_head, dout_heads, causal: bool, block: int = 256):
+    """dK and dV of every key of one KV head whose keys K are all zero,
+    float64 ([N, d], [N, d]); dQ is then exactly zero.
+
+    With K = 0 every score is 0, so row i attends uniformly to its visible
+    keys: P[i, j] = c_i = 1 / |J_i| (|J_i| = i + 1 causal, N otherwise).  The
+    chain rule of the module docstring then gives, with I_j the rows that
+    see key j (i >= j causal, all rows otherwise), O_i = c_i sum_{j in J_i}
+    V_j and D_i = dO_i . O_i:
+
+        dV_j = sum_{i in I_j} c_i dO_i
+        dS[i, j] = c_i (dO_i . V_j - D_i)
+        dK_j = (A_j V_j - b_j) / sqrt(d),
+            A_j = sum_{i in I_j} c_i Q_i dO_iᵀ,  b_j = sum_{i in I_j} c_i D_i Q_i
+
+    (summed over the G query heads in q_heads, dout_heads: [G, N, d]).  The
+    sums over I_j are suffix sums when causal, taken ``block`` rows at a time
+    from the last block down: O(N d^2) per head instead of the O(N^2 d) of
+    the general form, so it runs at the full sequence lengths.
+    """
+    q_heads, v_head, dout_heads = (_as_f64(x) for x in (q_heads, v_head, dout_heads))
+    G, N, d = q_heads.shape
+    scale = 1.0 / np.sqrt(d)
+    count = np.arange(1, N + 1, dtype=np.float64) if causal else np.full(N, float(N))
+    c = 1.0 / count
+    if causal:
+        o = np.cumsum(v_head, axis=0) * c[:, None]
+    else:
+        o = np.broadcast_to(v_head.sum(axis=0) * c[0], (N, d))
+    dk = np.zeros((N, d))
+    dv = np.zeros((N, d))
+    for h in range(G):
+        qh, doh = q_heads[h], dout_heads[h]
+        D = (doh * o).sum(axis=1)
+        cdo = doh * c[:, None]
+        if not causal:
+            A = qh.T @ cdo                       # sum_i c_i Q_i dO_iᵀ
+            b = qh.T @ (c * D)
+            dv += cdo.sum(axis=0)[None, :]
+            dk += (v_head @ A.T - b[None, :]) * scale
+            continue
+        dv += np.cumsum(cdo[::-1], axis=0)[::-1]
+        A = np.zeros((d, d))
+        b = np.zeros(d)
+        for j0 in range((N - 1) // block * block, -1, -block):
+            j1 = min(N, j0 + block)
+            rows = slice(j0, j1)
+            vb, qb, cdb = v_head[rows], qh[rows], cdo[rows]
+            # in-block rows i >= j: W[i, j] = c_i (dO_i . V_j - D_i)
+            w = cdb @ vb.T - (c[rows] * D[rows])[:, None]
+            w = np.tril(w)
+            dk[rows] += (vb @ A.T - b[None, :] + w.T @ qb) * scale
+            A += qb.T @ cdb
+            b += qb.T @ (c[rows] * D[rows])
+    return dk, dv

@@ -189,3 +189,46 @@ def test_sampled_forms_equal_full_backward(causal):
                                                causal, row_chunk=chunk)
             np.testing.assert_allclose(gk, dk[0, g, keys], rtol=1e-12, atol=1e-12)
             np.testing.assert_allclose(gv, dv[0, g, keys], rtol=1e-12, atol=1e-12)
+
+
+# ---- K = 0 closed form (full sequence lengths) against the full oracle ------
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 2, 300, 16), (4, 2, 257, 8), (1, 1, 1, 8), (2, 1, 513, 32)],
+                         ids=str)
+def test_zero_key_closed_form_equals_full_backward(shape, causal):
+    """backward_zero_keys (uniform attention over the visible keys, suffix
+    sums taken block by block) equals the general oracle with K = 0 on every
+    key, for ragged lengths and GQA, whatever the block; dQ is then zero."""
+    H_Q, H_KV, N, d = shape
+    rng = np.random.default_rng(N + d)
+    q = rng.standard_normal((1, H_Q, N, d))
+    v = rng.standard_normal((1, H_KV, N, d))
+    do = rng.standard_normal((1, H_Q, N, d))
+    k = np.zeros((1, H_KV, N, d))
+    dq, dk, dv = bwd_mod.attention_backward(q, k, v, do, causal)
+    assert np.all(dq == 0.0)
+    G = H_Q // H_KV
+    for g in range(H_KV):
+        heads = slice(g * G, (g + 1) * G)
+        for block in (1, 64, 256):
+            gk, gv = bwd_mod.backward_zero_keys(q[0, heads], v[0, g], do[0, heads], causal, block=block)
+            np.testing.assert_allclose(gk, dk[0, g], rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(gv, dv[0, g], rtol=1e-10, atol=1e-12)
+
+
+def test_zero_key_closed_form_is_sensitive():
+    """The comparison above discriminates: the causal closed form differs from
+    the non-causal oracle, and dK depends on V through the rows' D term (with
+    K = 0, V enters dK only through dO_i . V_j and D_i)."""
+    rng = np.random.default_rng(5)
+    H, N, d = 2, 130, 8
+    q = rng.standard_normal((1, H, N, d))
+    v = rng.standard_normal((1, H, N, d))
+    do = rng.standard_normal((1, H, N, d))
+    k = np.zeros((1, H, N, d))
+    _, dk, dv = bwd_mod.attention_backward(q, k, v, do, False)
+    gk, gv = bwd_mod.backward_zero_keys(q[0, :1], v[0, 0], do[0, :1], True)
+    assert not np.allclose(gk, dk[0, 0]) and not np.allclose(gv, dv[0, 0])
+    gk0, _ = bwd_mod.backward_zero_keys(q[0, :1], np.zeros_like(v[0, 0]), do[0, :1], False)
+    gk1, _ = bwd_mod.backward_zero_keys(q[0, :1], v[0, 0], do[0, :1], False)
+    assert not np.allclose(gk0, gk1)
