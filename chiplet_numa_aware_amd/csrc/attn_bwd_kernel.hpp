@@ -187,8 +187,9 @@ __device__ __forceinline__ void bwd_load_tile(u32x4 desc, int row0, int head_row
 // operands of S = Q K^T and dP = dO V^T) and the dK^T, dV^T accumulators sit
 // in AGPRs for the whole kernel.  The workgroup streams 32-row tiles of Q and
 // dO, of every query head of the KV group, through a ring of kDkvStages LDS
-// stages; a tile is loaded LDS-direct three tiles before its first use,
-// together with its rows' lse2 and D (one 256-byte copy per wave).
+// stages; tile t+3 is loaded LDS-direct during the body of tile t, one
+// instruction per bundle, together with its rows' lse2 and D (one 256-byte
+// copy per wave), and first read two bodies later.
 //
 // The body of tile t is one static schedule of MFMA "bundles":
 //   first part:  dV^T += dO^T P and dK^T += Q^T dS of tile t-1, while the
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
   // issued one instruction per bundle by issue_one<i>, i < LPT.
   struct LoadPlan {
     u32x4 q_desc, do_desc, st_desc;
-    uint32_t soff, st_voff, stage_off;
+    uint32_t soff, st_voff, stage;
   };
   auto plan = [&](int hg, int qt, int stage) {
     LoadPlan lp;
@@ -320,12 +321,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
     lp.st_desc = make_desc(ws + st_head0 + (uint64_t)hh * 2u * (uint64_t)N, (uint32_t)N * 8u);
     const int r = min(qt * kBwdTile + l32, N - 1);
     lp.st_voff = valid ? (uint32_t)(g * N + r) * 4u : kOutOfRange;
-    lp.stage_off = (uint32_t)stage;
+    lp.stage = (uint32_t)stage;
     return lp;
   };
   auto issue_one = [&](const LoadPlan& lp, auto ii) {
     constexpr int i = decltype(ii)::value;
-    const uint32_t stage = lp.stage_off;
+    const uint32_t stage = lp.stage;
     if constexpr (i < C::SLOTS)
       load_lds(lp.q_desc, slot_off[i], lp.soff,
                lds_base + stage * C::TILE_B + (wave + 4 * i) * 1024);
