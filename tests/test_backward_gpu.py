@@ -63,6 +63,24 @@ def test_backward_bitwise_identical_across_mappings(causal):
                 assert torch.equal(a, b), (mapping, name)
 
 
+def test_backward_workspace_layout_is_checked():
+    """The workspace is [B, H_Q, 2, N] (each head's lse2 rows, then its D
+    rows); a buffer of another shape, or on the host, is rejected before
+    any launch."""
+    B, H_Q, H_KV, N, d = 2, 4, 2, 64, 64
+    q, k, v, dout = grad_inputs(B, H_Q, H_KV, N, d, seed=925)
+    o, lse = attn.attn_fwd(q, k, v)
+    for bad in (torch.empty((2, B, H_Q, N), device="cuda"),
+                torch.empty((B, H_Q, 2, N)),
+                torch.empty((B, H_Q, 2, N), device="cuda", dtype=torch.float64)):
+        with pytest.raises(ValueError):
+            attn.attn_bwd(q, k, v, o, dout, lse, ws=bad)
+    dq, dk, dv = attn.attn_bwd(q, k, v, o, dout, lse, ws=torch.empty((B, H_Q, 2, N), device="cuda"))
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(f64(q), f64(k), f64(v), f64(dout), False)
+    check_grad(f64(dk), rk, "dK with a caller workspace")
+
+
 def test_backward_writes_every_element():
     """Outputs prefilled with NaN come back finite (every element written)."""
     B, H_Q, H_KV, N, d = 1, 4, 2, 390, 120
