@@ -415,6 +415,16 @@ def _recorded_commands(directory: str, workload: str, which: str = "fwd"):
     return profile_commands(workload, os.path.abspath(directory), which)
 
 
+def _headline_mode(modes, causal: bool) -> int:
+    """The mapping a bench line reports as its value: the binding's default
+    (swizzled head-first; with a causal mask also longest first and the
+    balanced split) when it was timed, else the closest one timed."""
+    for m in ((15, 7, 3) if causal else (3,)):
+        if m in modes:
+            return m
+    return modes[-1]
+
+
 def _same_box_bench(directory: str):
     """Per-mode results of the bench run recorded in DIR/bench.json (the
     profile's first command), or None."""
@@ -424,6 +434,34 @@ def _same_box_bench(directory: str):
     with open(path) as f:
         lines = [ln for ln in f.read().splitlines() if ln.strip()]
     return json.loads(lines[-1]).get("modes") if lines else None
+
+
+def _issue_summary(c) -> dict:
+    """Instructions per MFMA and the split of wave-cycles from one dispatch's
+    issue (SQ_INSTS_*) and waits (SQ_WAIT_*, SQ_ACTIVE_INST_ANY) counters."""
+    n_mfma = max(c["SQ_INSTS_MFMA"], 1.0)
+    return {
+        # SQ_INSTS_VALU counts the MFMAs too
+        "valu_per_mfma": round((c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"]) / n_mfma, 3),
+        "salu_per_mfma": round(c["SQ_INSTS_SALU"] / n_mfma, 3),
+        "lds_per_mfma": round(c["SQ_INSTS_LDS"] / n_mfma, 3),
+        "active_inst_pct": round(100.0 * c["SQ_ACTIVE_INST_ANY"] / c["SQ_WAVE_CYCLES"], 2),
+        "wait_any_pct": round(100.0 * c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"], 2),
+        "wait_inst_any_pct": round(100.0 * c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"], 2),
+    }
+
+
+ISSUE_TABLE_HEAD = [
+    "Instructions per MFMA (SQ_INSTS_*; VALU without the MFMAs) and the share of wave-cycles "
+    "spent issuing (SQ_ACTIVE_INST_ANY), waiting on s_waitcnt or a barrier (SQ_WAIT_ANY) and "
+    "waiting to issue (SQ_WAIT_INST_ANY), of SQ_WAVE_CYCLES.", "",
+    "| mode | VALU / MFMA | SALU / MFMA | LDS / MFMA | issuing % | waitcnt+barrier % | issue-wait % |",
+    "|---|---|---|---|---|---|---|"]
+
+
+def _issue_row(name, i) -> str:
+    return (f"| {name} | {i['valu_per_mfma']} | {i['salu_per_mfma']} | {i['lds_per_mfma']} | "
+            f"{i['active_inst_pct']} | {i['wait_any_pct']} | {i['wait_inst_any_pct']} |")
 
 
 def summarize_profile(directory: str, workload: str):
@@ -487,17 +525,7 @@ def summarize_profile(directory: str, workload: str):
         }
         entry = modes[MODE_NAMES[PROFILE_MODES[m]]]
         if iss is not None and len(iss) == n_modes:
-            c = iss[m]
-            n_mfma = max(c["SQ_INSTS_MFMA"], 1.0)
-            entry["issue"] = {
-                # SQ_INSTS_VALU counts the MFMAs too
-                "valu_per_mfma": round((c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"]) / n_mfma, 3),
-                "salu_per_mfma": round(c["SQ_INSTS_SALU"] / n_mfma, 3),
-                "lds_per_mfma": round(c["SQ_INSTS_LDS"] / n_mfma, 3),
-                "active_inst_pct": round(100.0 * c["SQ_ACTIVE_INST_ANY"] / c["SQ_WAVE_CYCLES"], 2),
-                "wait_any_pct": round(100.0 * c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"], 2),
-                "wait_inst_any_pct": round(100.0 * c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"], 2),
-            }
+            entry["issue"] = _issue_summary(iss[m])
         if same_box and MODE_NAMES[PROFILE_MODES[m]] in same_box:
             sb = same_box[MODE_NAMES[PROFILE_MODES[m]]]
             entry["same_box_bench"] = {"kernel_ms_avg": sb["kernel_ms_avg"],
@@ -551,17 +579,10 @@ def summarize_profile(directory: str, workload: str):
                 lines.append(f"| {name} | {sb['kernel_ms_avg']:.2f} | {sb['tflops']} | {sb['frac_of_peak']} |")
         lines.append("")
     if any("issue" in mm for mm in modes.values()):
-        lines += ["## Where the non-MFMA time goes (SQ counters, one dispatch per mode)", "",
-                  "Instructions per MFMA (SQ_INSTS_*; VALU without the MFMAs) and the share of wave-cycles "
-                  "spent issuing (SQ_ACTIVE_INST_ANY), waiting on s_waitcnt or a barrier (SQ_WAIT_ANY) and "
-                  "waiting to issue (SQ_WAIT_INST_ANY), of SQ_WAVE_CYCLES.", "",
-                  "| mode | VALU / MFMA | SALU / MFMA | LDS / MFMA | issuing % | waitcnt+barrier % | issue-wait % |",
-                  "|---|---|---|---|---|---|---|"]
+        lines += ["## Where the non-MFMA time goes (SQ counters, one dispatch per mode)", ""] + ISSUE_TABLE_HEAD
         for name, mm in modes.items():
             if "issue" in mm:
-                i = mm["issue"]
-                lines.append(f"| {name} | {i['valu_per_mfma']} | {i['salu_per_mfma']} | {i['lds_per_mfma']} | "
-                             f"{i['active_inst_pct']} | {i['wait_any_pct']} | {i['wait_inst_any_pct']} |")
+                lines.append(_issue_row(name, mm["issue"]))
         lines.append("")
     lines += ["## Commands", ""]
     lines.append("Each pass is its own process, run as `cd /tmp && export TMPDIR=/tmp && <command>` "
@@ -609,6 +630,13 @@ def summarize_bwd_profile(directory: str, workload: str):
         mf, mdur = one("mfma", kern)
         if not (len(l2) == len(fe) == len(wr) == len(mf) == len(PROFILE_MODES)):
             raise SystemExit(f"expected one {kern} dispatch per mapping mode in every pass")
+        iss = None
+        if (glob.glob(os.path.join(directory, "issue", "*_counter_collection.csv"))
+                and glob.glob(os.path.join(directory, "waits", "*_counter_collection.csv"))):
+            ia, _ = one("issue", kern)
+            ib, _ = one("waits", kern)
+            if len(ia) == len(ib) == len(PROFILE_MODES):
+                iss = [dict(a, **b) for a, b in zip(ia, ib)]
         rows = {}
         for m in range(len(PROFILE_MODES)):
             hit, miss = l2[m]["TCC_HIT_sum"], l2[m]["TCC_MISS_sum"]
@@ -623,6 +651,8 @@ def summarize_bwd_profile(directory: str, workload: str):
                 "clock_ghz": round(gui / 8.0 / mdur[m] / 1e9, 3),
                 "kernel_ms_counter_run": round(durs[m] * 1e3, 3),
             }
+            if iss is not None:
+                rows[MODE_NAMES[PROFILE_MODES[m]]]["issue"] = _issue_summary(iss[m])
         per_kernel[kern] = rows
     modes = {}
     for m, mode in enumerate(PROFILE_MODES):
@@ -630,6 +660,15 @@ def summarize_bwd_profile(directory: str, workload: str):
         total = pre_durs[m] * 1e3 + sum(per_kernel[k][name]["kernel_ms_counter_run"] for k in per_kernel)
         modes[name] = {"ms": round(total, 3), "tflops": round(flops / (total / 1e3) / 1e12, 1),
                        "pre_ms": round(pre_durs[m] * 1e3, 3)}
+    same_box = _same_box_bench(directory)
+    if same_box:
+        for name in modes:
+            if name in same_box:
+                sb = same_box[name]
+                modes[name]["same_box_bench"] = {
+                    "kernel_ms_avg": sb["kernel_ms_avg"],
+                    "tflops": round(flops / (sb["kernel_ms_avg"] / 1e3) / 1e12, 1),
+                    "frac_of_peak": round(flops / (sb["kernel_ms_avg"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     trace = glob.glob(os.path.join(directory, "trace", "*_kernel_stats.csv"))
     stats = []
     if trace:
@@ -660,6 +699,22 @@ def summarize_bwd_profile(directory: str, workload: str):
               "| mode | ms | TFLOP/s | % of bf16 peak |", "|---|---|---|---|"]
     for name, mm in modes.items():
         lines.append(f"| {name} | {mm['ms']} | {mm['tflops']} | {100 * mm['tflops'] / PEAK_BF16_TFLOPS:.1f} |")
+    if any("same_box_bench" in mm for mm in modes.values()):
+        lines += ["", "## Same-box benchmark (bench.py on the profiled box, before the profiler runs)", "",
+                  f"HIP-event mean time of one attn_bwd call (its three kernels); TFLOP/s = "
+                  f"{flops / 1e12:.1f} TFLOP / time; fraction of the {PEAK_BF16_TFLOPS:.0f} TFLOP/s bf16 peak.", "",
+                  "| mode | ms | TFLOP/s | frac of peak |", "|---|---|---|---|"]
+        for name, mm in modes.items():
+            if "same_box_bench" in mm:
+                sb = mm["same_box_bench"]
+                lines.append(f"| {name} | {sb['kernel_ms_avg']:.2f} | {sb['tflops']} | {sb['frac_of_peak']} |")
+    for kern, rows in per_kernel.items():
+        if any("issue" in mm for mm in rows.values()):
+            lines += ["", f"## {kern}, where the non-MFMA time goes (SQ counters, one dispatch per mode)", ""]
+            lines += ISSUE_TABLE_HEAD
+            for name, mm in rows.items():
+                if "issue" in mm:
+                    lines.append(_issue_row(name, mm["issue"]))
     for kern, rows in per_kernel.items():
         lines += ["", f"## {kern}, counters per mapping mode (one dispatch each)", "",
                   "| mode | L2 hit % | HBM read GB | HBM write GB | read / unique | MFMA busy % | clock GHz | ms |",
@@ -687,7 +742,7 @@ def run_bwd(args, attn, inputs):
     import torch
     B, H_Q, H_KV, N, d, causal = WORKLOADS[args.workload]
     modes = [int(m) for m in args.modes.split(",") if m.strip() != ""]
-    headline = 7 if (causal and 7 in modes) else (3 if 3 in modes else modes[-1])
+    headline = _headline_mode(modes, causal)
     flops = pass_flops("bwd", B, H_Q, N, d, causal)
     log(f"workload {describe(args.workload)} backward: {flops / 1e12:.1f} TFLOP per call")
     q, k, v = inputs.make_qkv(B, H_Q, H_KV, N, d, seed=1000, device="cuda")
@@ -1219,8 +1274,9 @@ def main():
                     help="default: mha_128k (gemm_tall_64k_2k_8k for --pass gemm, "
                          "decode_gqa64x8_b16_128k for --pass decode)")
     ap.add_argument("--modes", default="0,1,2,3",
-                    help="mapping modes to time; the last one listed that is "
-                         "3 (or the last one) is the headline")
+                    help="mapping modes to time; the headline is the binding's "
+                         "default (3, or 15 with a causal mask; else 7 or 3) when "
+                         "listed, else the last one")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "gemm", "decode"), default="fwd",
                     help="fwd: attn_fwd (default); bwd: attn_bwd on the forward's O, lse; "
                          "gemm: cac_gemm (workloads gemm_*); decode: attn_fwd_split "
@@ -1300,7 +1356,7 @@ def main():
         return
     B, H_Q, H_KV, N, d, causal = WORKLOADS[args.workload]
     modes = [int(m) for m in args.modes.split(",") if m.strip() != ""]
-    headline = 3 if 3 in modes else modes[-1]
+    headline = _headline_mode(modes, causal)
     flops = attn_flops(B, H_Q, N, d, causal)
     log(f"workload {describe(args.workload)}: {flops / 1e12:.1f} TFLOP per call")
 
