@@ -409,8 +409,12 @@ def _recorded_commands(directory: str, workload: str, which: str = "fwd"):
     by --print-profile-commands, else the commands for that directory."""
     path = os.path.join(directory, "commands.txt")
     if os.path.exists(path):
+        import re
         with open(path) as f:
-            cmds = [line.strip() for line in f if line.strip()]
+            # /root/repo is a link to wherever the run's copy of the
+            # repository lived; name the output paths through it
+            cmds = [re.sub(r"/\S*?/repo/gpurun_out/", "/root/repo/gpurun_out/", line.strip())
+                    for line in f if line.strip()]
         return dict(zip(profile_commands(workload, "X", which).keys(), cmds))
     return profile_commands(workload, os.path.abspath(directory), which)
 
