@@ -303,23 +303,48 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
   });
   // The loads of tile (hg, qt) into stage `stage`: descriptors and offsets
   // (a tile past the sequence, hg == G, reads nothing and writes zeros),
-  // issued one instruction per bundle by issue_one<i>, i < LPT.
+  // issued one instruction per bundle by issue_one<i>, i < LPT.  A cursor
+  // keeps the next tile's descriptors and offsets: a tile step adds the tile
+  // stride to the offsets, and only a step to the next query head moves the
+  // descriptors (scalar 64-bit arithmetic once per head, not per tile).
   struct LoadPlan {
     u32x4 q_desc, do_desc, st_desc;
     uint32_t soff, st_voff, stage;
   };
-  auto plan = [&](int hg, int qt, int stage) {
+  // Cursor of the next tile to load: its query head c_hg, row tile c_qt and
+  // the descriptors of that head, moved only when the head changes (the
+  // scalar 64-bit address arithmetic then runs once per head, not per tile).
+  u32x4 c_qd = make_desc(q + q_head0, head_bytes);
+  u32x4 c_dod = make_desc(dout + q_head0, head_bytes);
+  u32x4 c_std = make_desc(ws + st_head0, (uint32_t)N * 8u);
+  int c_hg = 0, c_qt = qt0;
+  auto desc_add = [](u32x4& dsc, uint64_t bytes) {
+    const uint64_t a = ((uint64_t)(dsc.y & 0xFFFFu) << 32 | dsc.x) + bytes;
+    dsc.x = (uint32_t)a;
+    dsc.y = (uint32_t)(a >> 32) & 0xFFFFu;
+  };
+  auto advance = [&]() {
+    if (++c_qt == nq) {
+      c_qt = qt0;
+      // Past the last head the descriptors stay on it; validity then comes
+      // from c_hg alone.
+      if (++c_hg < G) {
+        desc_add(c_qd, (uint64_t)head_elems * 2u);
+        desc_add(c_dod, (uint64_t)head_elems * 2u);
+        desc_add(c_std, (uint64_t)N * 8u);
+      }
+    }
+  };
+  auto plan = [&](int stage) {
     LoadPlan lp;
-    const bool valid = hg < G;
-    const int hh = valid ? hg : 0;
-    const uint64_t qo = q_head0 + (uint64_t)hh * head_elems;
-    lp.q_desc = make_desc(q + qo, head_bytes);
-    lp.do_desc = make_desc(dout + qo, head_bytes);
-    const uint32_t soff0 = (uint32_t)(qt * kBwdTile) * (uint32_t)dd * 2u;
+    const bool valid = c_hg < G;
+    lp.q_desc = c_qd;
+    lp.do_desc = c_dod;
+    const uint32_t soff0 = (uint32_t)(c_qt * kBwdTile) * (uint32_t)dd * 2u;
     lp.soff = (valid && soff0 < head_bytes) ? soff0 : head_bytes;
     // Stats: lanes 0-31 lse2 of rows qt*32 + l32, lanes 32-63 their D.
-    lp.st_desc = make_desc(ws + st_head0 + (uint64_t)hh * 2u * (uint64_t)N, (uint32_t)N * 8u);
-    const int r = min(qt * kBwdTile + l32, N - 1);
+    lp.st_desc = c_std;
+    const int r = min(c_qt * kBwdTile + l32, N - 1);
     lp.st_voff = valid ? (uint32_t)(g * N + r) * 4u : kOutOfRange;
     lp.stage = (uint32_t)stage;
     return lp;
@@ -337,8 +362,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
       load_lds_dword(lp.st_desc, lp.st_voff,
                      lds_base + L::ST0 + stage * L::ST_STAGE + wave * 256);
   };
-  auto issue = [&](int hg, int qt, int stage) {
-    const LoadPlan lp = plan(hg, qt, stage);
+  auto issue = [&](int stage) {
+    const LoadPlan lp = plan(stage);
     static_for<L::LPT>([&](auto ii) { issue_one(lp, ii); });
   };
 
@@ -412,16 +437,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
 
   // ---- Prologue: tiles 0-2 in flight, tiles 0 and 1 waited for; S and dP
   // of tile 0; P = dS = 0 for "tile -1" (its stage is zero).
-  int hg_l = 0, qt_l = qt0;  // next tile to load
-  auto advance = [&](int& hg, int& qt) {
-    if (++qt == nq) {
-      qt = qt0;
-      ++hg;
-    }
-  };
   static_for<3>([&](auto si) {
-    issue(hg_l, qt_l, decltype(si)::value);
-    advance(hg_l, qt_l);
+    issue(decltype(si)::value);
+    advance();
   });
   wait_vmcnt<L::LPT>();
   barrier();
@@ -456,8 +474,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
   auto body = [&](auto phi, bool masked, int span) {
     constexpr int PH = decltype(phi)::value;
     constexpr int s_load = (PH + 3) % kDkvStages, s_next = (PH + 1) % kDkvStages;
-    const LoadPlan lp = plan(hg_l, qt_l, s_load);
-    advance(hg_l, qt_l);
+    const LoadPlan lp = plan(s_load);
+    advance();
     xdl_guard_v(s_cur, dp_cur);
     // A masked element gets S = -inf, hence P = 0 and dS = 0.
     if (masked) {
