@@ -303,10 +303,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
   });
   // The loads of tile (hg, qt) into stage `stage`: descriptors and offsets
   // (a tile past the sequence, hg == G, reads nothing and writes zeros),
-  // issued one instruction per bundle by issue_one<i>, i < LPT.  A cursor
-  // keeps the next tile's descriptors and offsets: a tile step adds the tile
-  // stride to the offsets, and only a step to the next query head moves the
-  // descriptors (scalar 64-bit arithmetic once per head, not per tile).
+  // issued one instruction per bundle by issue_one<i>, i < LPT.
   struct LoadPlan {
     u32x4 q_desc, do_desc, st_desc;
     uint32_t soff, st_voff, stage;
