@@ -31,6 +31,8 @@ CASES = [
     (1, 2, 2, 129, 64, True),      # one key past a 128-key block
     (1, 8, 2, 700, 128, True),     # GQA 4 heads per KV head, several blocks
     (1, 1, 1, 1030, 128, False),
+    (2, 6, 2, 301, 128, True),     # GQA, 3 query heads per KV head
+    (1, 3, 1, 190, 64, False),
 ]
 
 

@@ -58,6 +58,8 @@ SMALL = [
     (1, 8, 8, 2048, 128, True),
     (3, 6, 3, 384, 96, False),
     (1, 12, 12, 1100, 128, True),
+    (1, 6, 2, 333, 128, True),      # GQA, 3 query heads per KV head
+    (2, 9, 3, 70, 64, False),
 ]
 
 
