@@ -797,7 +797,8 @@ def run_bwd(args, attn, inputs):
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(head["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
-                     "scope": "one attn_bwd call (its three kernels, one stream)"},
+                     "scope": "one attn_bwd call (its three kernels, one stream)",
+                     "executed": _bwd_executed(head["kernel_tflops"], d)},
         "kernel_hash": kernel_hash("bwd"),
         "counters_source": counters_source(args.workload, kernel_hash("bwd"), "bwd", counters),
     }
@@ -805,6 +806,16 @@ def run_bwd(args, attn, inputs):
         out["speedup_vs_naive_block_first"] = round(
             results[0]["kernel_ms_avg"] / head["kernel_ms_avg"], 4)
     emit(out, args)
+
+
+def _bwd_executed(credited_tflops: float, d: int) -> dict:
+    """The MFMA work attn_bwd executes: per (query, visible key) 8 D_PAD FLOP
+    in the dK/dV kernel (S, dP, dV, dK) and 6 D_PAD in the dQ kernel (S and
+    dP again, dQ), against the 10 d credited (2.5x the forward's 4 d)."""
+    d_pad = 64 if d <= 64 else 128
+    ex = credited_tflops * 14.0 * d_pad / (10.0 * d)
+    return {"tflops": round(ex, 2), "frac": round(ex / PEAK_BF16_TFLOPS, 4),
+            "flop_per_pair": f"14 x {d_pad} executed against 10 x {d} credited"}
 
 
 def gemm_describe(name) -> str:

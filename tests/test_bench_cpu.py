@@ -112,3 +112,15 @@ def test_summarize_profile_arithmetic(tmp_path, monkeypatch):
         assert mm["clock_ghz"] == pytest.approx(2.0, abs=1e-3)
     md = open(out_dir / "attn_fwd_mha_h8_1k.md").read()
     assert re.search(r"Kernel source hash [0-9a-f]{16}", md)
+
+
+def test_backward_executed_work():
+    """attn_bwd executes 14 MFMA FLOP per (query, visible key) per padded
+    head dimension (S, dP, dV, dK; then S, dP and dQ again) against the
+    10 d credited, so at d = 128 the executed rate is 1.4x the credited one,
+    and at d = 56 (run on 64 padded columns) 1.6x."""
+    e = bench._bwd_executed(1000.0, 128)
+    assert e["tflops"] == pytest.approx(1400.0)
+    assert e["frac"] == pytest.approx(1400.0 / bench.PEAK_BF16_TFLOPS, abs=1e-4)
+    assert bench._bwd_executed(1000.0, 56)["tflops"] == pytest.approx(1600.0)
+    assert bench._bwd_executed(1000.0, 96)["tflops"] == pytest.approx(1000.0 * 14 * 128 / 960)
