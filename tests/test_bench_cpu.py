@@ -123,4 +123,4 @@ def test_backward_executed_work():
     assert e["tflops"] == pytest.approx(1400.0)
     assert e["frac"] == pytest.approx(1400.0 / bench.PEAK_BF16_TFLOPS, abs=1e-4)
     assert bench._bwd_executed(1000.0, 56)["tflops"] == pytest.approx(1600.0)
-    assert bench._bwd_executed(1000.0, 96)["tflops"] == pytest.approx(1000.0 * 14 * 128 / 960)
+    assert bench._bwd_executed(1000.0, 96)["tflops"] == pytest.approx(1000.0 * 14 * 128 / 960, abs=0.01)
