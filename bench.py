@@ -919,6 +919,13 @@ def summarize_gemm_profile(directory: str, workload: str):
     mf, mdur = one("mfma", "cac_gemm_kernel")
     if not (len(l2) == len(fe) == len(wr) == len(mf) == 4):
         raise SystemExit("expected one cac_gemm dispatch per tile map in every pass")
+    iss = None
+    if (glob.glob(os.path.join(directory, "issue", "*_counter_collection.csv"))
+            and glob.glob(os.path.join(directory, "waits", "*_counter_collection.csv"))):
+        ia, _ = one("issue", "cac_gemm_kernel")
+        ib, _ = one("waits", "cac_gemm_kernel")
+        if len(ia) == len(ib) == 4:
+            iss = [dict(x, **y) for x, y in zip(ia, ib)]
     unique = 2 * L * (M * K + N * K + M * N)
     modes = {}
     for m in range(4):
@@ -938,6 +945,8 @@ def summarize_gemm_profile(directory: str, workload: str):
             # without the power-limit clock of each run
             "tflops_per_ghz": round(flops / durs[m] / 1e12 / (gui / 8.0 / mdur[m] / 1e9), 1),
         }
+        if iss is not None:
+            modes[GEMM_MODE_NAMES[m]]["issue"] = _issue_summary(iss[m])
     same_box = _same_box_bench(directory)
     if same_box:
         for name, mm in modes.items():
@@ -974,7 +983,14 @@ def summarize_gemm_profile(directory: str, workload: str):
                      f"{mm['clock_ghz']} | {mm['kernel_ms_counter_run']} | {mm['tflops_counter_run']} | "
                      f"{mm['tflops_per_ghz']} | {mm.get('same_box_bench_tflops', '')} |")
     lines += ["", f"HBM bytes: FETCH_SIZE and WRITE_SIZE scaled by a plain 1 GiB copy's counts "
-              f"(read x{cal['FETCH_SIZE']:.3f}, write x{cal['WRITE_SIZE']:.3f}).", "", "## Commands", "",
+              f"(read x{cal['FETCH_SIZE']:.3f}, write x{cal['WRITE_SIZE']:.3f}).", ""]
+    if any("issue" in mm for mm in modes.values()):
+        lines += ["## Where the non-MFMA time goes (SQ counters, one dispatch per tile map)", ""] + ISSUE_TABLE_HEAD
+        for name, mm in modes.items():
+            if "issue" in mm:
+                lines.append(_issue_row(name, mm["issue"]))
+        lines.append("")
+    lines += ["## Commands", "",
               "Each pass is its own process, run as `cd /tmp && export TMPDIR=/tmp && <command>` "
               "with the repository at /root/repo; then "
               f"`python3 bench.py --workload {workload} --pass gemm --summarize-profile DIR` wrote this file.", ""]
