@@ -339,3 +339,17 @@ def test_noalloc_rejects_oversize_before_touching_a_device(lib):
     assert n(d=12) == c["ATTN_E_HEAD_DIM"]
     # fits: validation passes the size check and stops at the missing GPU
     assert n(S=8, N_q=1) == c["ATTN_E_NO_DEVICE"]
+
+
+def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
+    """Without the built library every entry point fails loudly: there is no
+    CPU path to fall back to."""
+    monkeypatch.setattr(attn, "LIB_PATH", str(tmp_path / "libattn_numa.so"))
+    monkeypatch.setattr(attn, "_lib", None)
+    with pytest.raises(RuntimeError, match="is not built"):
+        attn.load_library()
+    # A host tensor is refused as well (no CPU path computes attention).
+    import torch
+    q = torch.zeros((1, 1, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises((RuntimeError, ValueError)):
+        attn.attn_fwd(q, q, q)
