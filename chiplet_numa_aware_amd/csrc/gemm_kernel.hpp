@@ -7,11 +7,14 @@
 //
 // One workgroup computes one 256 x 256 tile of C with 8 waves (two per
 // SIMD, so one wave's LDS waits hide behind the other's MFMAs); wave w owns
-// rows 64 (w / 2) .. +64 and columns 128 (w % 2) .. +128 as 2 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16.  Each block is computed transposed,
-// C^T = B A^T (A operand: 32 columns of B; B operand: 32 rows of A), so a
-// lane's 16 accumulators are 4 runs of 4 consecutive columns of one C row and
-// the epilogue writes 8-byte pieces.  K advances 64 at a time; the A and B
+// rows 64 (w / 2) .. +64 and columns 128 (w % 2) .. +128 as 4 x 8 blocks of
+// v_mfma_f32_16x16x32_bf16.  For the same work this shape draws less power
+// than 32x32x16 (measured: the same FLOPs on random operands sustain 2.16
+// against 1.89-1.95 GHz under the chip's power limit), and the kernel runs
+// 2-7% faster with it.  Each block is computed transposed, C^T = B A^T
+// (A operand: 16 columns of B; B operand: 16 rows of A), so a lane's 4
+// accumulators are 4 consecutive columns of one C row and the epilogue
+// writes 8-byte pieces.  K advances 64 at a time; the A and B
 // slices of a K step go from global memory straight into LDS (buffer loads
 // with the LDS-direct bit), two stages deep, so a step's loads have one step
 // of MFMAs (two waves per SIMD) to land.  An LDS slice is 256 rows of K-step / 8 16-byte
@@ -28,6 +31,8 @@
 #include "cac_map.hpp"
 
 namespace attn_numa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmTile = 256;   // rows and columns of a C tile
 // K per step: 64 with two stages measured 3-10% faster than 32 with four
@@ -63,7 +68,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void cac_gemm_kernel(
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lb);
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int g = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const TileCoord tc = cac_tile_map(mapping, blockIdx.x, L, Mt, Nt, gm, gn, num_xcd);
   const int m0 = (int)tc.tm * kGemmTile, n0 = (int)tc.tn * kGemmTile;
@@ -104,18 +108,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void cac_gemm_kernel(
     }
   };
 
-  // Operand reads: lane (row l32 of a 32-row block, half g) reads chunk
-  // 2 kc + g of its row.
-  int rd[kGemmKC];
+  // Operand reads (v_mfma_f32_16x16x32_bf16): lane (row r16 of a 16-row
+  // block, quarter q) reads chunk 4 k32 + q of its row; the 16 lanes of a
+  // quarter read 16 consecutive rows of one chunk.
+  constexpr int kK32 = kGemmBK / 32;  // 32-deep MFMA steps per K step
+  const int r16 = lane & 15, q4 = lane >> 4;
+  int rd[kK32];
 #pragma unroll
-  for (int kc = 0; kc < kGemmKC; ++kc) rd[kc] = l32 * kGemmRowB + (((2 * kc + g) ^ gemm_swz(l32)) * 16);
+  for (int kc = 0; kc < kK32; ++kc) rd[kc] = r16 * kGemmRowB + (((4 * kc + q4) ^ gemm_swz(r16)) * 16);
   const int wm = 64 * (wave >> 1), wn = 128 * (wave & 1);
 
-  f32x16 acc[2][4];
+  f32x4 acc[4][8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{};
 
   // Prologue: steps 0 .. stages-2 in flight.
 #pragma unroll
@@ -137,47 +144,44 @@ __global__ __launch_bounds__(kGemmThreads, 1) void cac_gemm_kernel(
     // wait only for its own fragments, and chunk 1's arrive meanwhile.
     const char* sa = lb + (step & (kGemmStages - 1)) * kGemmStageB;
     const char* sb = sa + kGemmSliceB;
-    bf16x8 fa[kGemmKC][2], fb[kGemmKC][4];
+    bf16x8 fa[kK32][4], fb[kK32][8];
 #pragma unroll
-    for (int kc = 0; kc < kGemmKC; ++kc) {
+    for (int kc = 0; kc < kK32; ++kc) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[kc][i] = *reinterpret_cast<const bf16x8*>(sa + (wm + 32 * i) * kGemmRowB + rd[kc]);
+      for (int i = 0; i < 4; ++i)
+        fa[kc][i] = *reinterpret_cast<const bf16x8*>(sa + (wm + 16 * i) * kGemmRowB + rd[kc]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[kc][j] = *reinterpret_cast<const bf16x8*>(sb + (wn + 32 * j) * kGemmRowB + rd[kc]);
+      for (int j = 0; j < 8; ++j)
+        fb[kc][j] = *reinterpret_cast<const bf16x8*>(sb + (wn + 16 * j) * kGemmRowB + rd[kc]);
     }
     // The stage written next was last read in step - 1, which every wave
     // finished before the barrier above.
     if (step + kGemmStages - 1 < n_steps) issue(step + kGemmStages - 1);
 #pragma unroll
-    for (int kc = 0; kc < kGemmKC; ++kc)
+    for (int kc = 0; kc < kK32; ++kc)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kc][j], fa[kc][i], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6 * kGemmKC, 0);  // the LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 8 * kGemmKC, 0);  // then the MFMAs
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[kc][j], fa[kc][i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12 * kK32, 0);  // the LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 32 * kK32, 0);  // then the MFMAs
   }
 
-  // acc[i][j] register r: C row m0 + wm + 32 i + l32, column
-  // n0 + wn + 32 j + 8 (r / 4) + 4 g + (r % 4).
+  // acc[i][j] register r (16x16 block, computed transposed as C^T = B A^T):
+  // C row m0 + wm + 16 i + r16, column n0 + wn + 16 j + 4 q4 + r.
   const __amdgpu_buffer_rsrc_t c_rs = make_rsrc(c + (uint64_t)tc.l * M * N, c_bytes);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = m0 + wm + 32 * i + l32;
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + wm + 16 * i + r16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int col = n0 + wn + 32 * j + 8 * rr + 4 * g;
-        if (row < M && col < N) {
-          u32x2 w;
-          w.x = pack_bf16x2(acc[i][j][4 * rr + 0], acc[i][j][4 * rr + 1]);
-          w.y = pack_bf16x2(acc[i][j][4 * rr + 2], acc[i][j][4 * rr + 3]);
-          __builtin_amdgcn_raw_buffer_store_b64(w, c_rs, ((uint32_t)row * (uint32_t)N + col) * 2u, 0, 0);
-        }
+    for (int j = 0; j < 8; ++j) {
+      const int col = n0 + wn + 16 * j + 4 * q4;
+      if (row < M && col < N) {
+        u32x2 w;
+        w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        __builtin_amdgcn_raw_buffer_store_b64(w, c_rs, ((uint32_t)row * (uint32_t)N + col) * 2u, 0, 0);
       }
     }
   }
