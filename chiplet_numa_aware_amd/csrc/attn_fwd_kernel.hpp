@@ -10,12 +10,6 @@
 // ("Fused Grouped-Query Attention" page, the decode reduction of per-shard
 // partial results).
 //
-// This template is instantiated for padded head dim 64 (d <= 64); head dims
-// 65..128 run attn_fwd_kernel_m16 (attn_fwd16_kernel.hpp), which keeps this
-// workgroup, load pipeline and running-max protocol on 16 x 16 MFMA blocks.
-// The D = 128 form of this template is kept compilable; measured against the
-// 16 x 16 kernel it was 1-2.5% slower at N = 128K.
-//
 // Work inside a workgroup (256 threads = 4 waves of 64; one wave per SIMD,
 // one workgroup per CU):
 //   * wave w owns query rows [64w, 64w+64) of the block as two 32-row query
