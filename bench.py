@@ -30,7 +30,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "fwd": ["chiplet_numa_aware_amd/csrc/attn_fwd_kernel.hpp",
-            "chiplet_numa_aware_amd/csrc/attn_fwd16_kernel.hpp",
             "chiplet_numa_aware_amd/csrc/wg_map.hpp",
             "chiplet_numa_aware_amd/csrc/fwd_launch.hpp",
             "chiplet_numa_aware_amd/csrc/attn_fwd_d64.hip",

@@ -1,10 +1,9 @@
 // Forward kernel instantiations for padded head dim 128 (causal x d == D),
 // in a translation unit of their own so the two head dims compile in
-// parallel.  Head dims 65..128 run the 16 x 16 MFMA kernel
-// (attn_fwd16_kernel.hpp); head dims up to 64 run attn_fwd_kernel<64>.
+// parallel.
 #include <hip/hip_runtime.h>
 
-#include "attn_fwd16_kernel.hpp"
+#include "attn_fwd_kernel.hpp"
 #include "fwd_launch.hpp"
 
 namespace attn_numa {
@@ -12,8 +11,7 @@ namespace {
 
 template <int D, bool CAUSAL, bool FULL_D>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
-  static_assert(D == 128, "the 16 x 16 kernel pads the head dim to 128");
-  hipLaunchKernelGGL((attn_fwd_kernel_m16<CAUSAL, FULL_D>), dim3(a.W), dim3(kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, FULL_D>), dim3(a.W), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o),
