@@ -273,7 +273,7 @@ struct TileCfg {
 // in proportion to their cost (4-cycle units; fma + exp2 counts 3) over the
 // bundles before the last chunk's deadline, and the max steps, which need
 // the score MFMAs, over the bundles after it.
-template <int D>
+template <int D, bool ONES = false>
 struct TileSchedule {
   using C = TileCfg<D>;
   static constexpr int NS = C::KC * kQB;
@@ -293,7 +293,7 @@ struct TileSchedule {
   static constexpr int cost(int s) {
     if (s >= EXP_STEPS) return 1;
     const int k = s % STEPS_PER_CHUNK;
-    return k < 8 ? 3 : (k < 12 ? 1 : 2);
+    return k < 8 ? 3 : (k < 12 ? 1 : (ONES ? 0 : 2));
   }
   static constexpr int cost_before(int s) {
     int c = 0;
@@ -330,7 +330,11 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void attn_fwd_kernel(
     int N_kv, int d, int M_q, int kv_chunk, int num_splits, float* __restrict__ o_ws,
     float* __restrict__ lse_ws, int mapping, int num_xcd, float scale_log2) {
   using C = TileCfg<D>;
-  using TS = TileSchedule<D>;
+  // d < D: the last 16-byte chunk of every V row is padding; its first
+  // element is set to 1 in LDS, so the P V MFMA accumulates the row sum of
+  // the bf16 P in O^T row D - 8 (block DB - 1, element 12 of lanes 0-31).
+  constexpr bool kOnes = !FULL_D;
+  using TS = TileSchedule<D, kOnes>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[C::LDS_B / 4];
   char* const lds_b = reinterpret_cast<char*>(lds);
   // K buffers at [0, kStages * TILE_B), V buffers after them.
@@ -441,6 +445,19 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void attn_fwd_kernel(
   const uint32_t m0_wave = lds_base + (uint32_t)wave_blk0 * 1024u;
   auto k_buf = [&](int tile) { return (tile & (kStages - 1)) * C::TILE_B; };
   auto v_buf = [&](int tile) { return kVBase + (tile & (kStages - 1)) * C::TILE_B; };
+  // d < D: element D - 8 (the first of the padding chunk) of every row of V
+  // tile `vbuf_byte` set to 1.  A tile load may rewrite the padding chunk
+  // with zeros, so each tile sets it again after the barrier that made its
+  // loads visible and before any read of the tile; every wave writes the 32
+  // rows itself (identical values), so no other barrier is needed.
+  auto ones_col = [&](int vbuf_byte) {
+    if constexpr (kOnes) {
+      if (lane < kBlockN) {
+        const int slot = (C::CPR - 1) ^ (lane & 7);
+        *reinterpret_cast<uint16_t*>(lds_b + vbuf_byte + lane * C::ROWB + slot * 16) = 0x3F80u;
+      }
+    }
+  };
   // Byte offset of a tile, capped at the head size: a tile past the end then
   // reads nothing, and soff + kOutOfRange stays below 2^32.
   auto tile_soff = [&](int tile) {
@@ -572,7 +589,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void attn_fwd_kernel(
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           pk[qb][w] = pack_bf16x2(p[2 * w], p[2 * w + 1]);
-          l_run[qb] += p[2 * w] + p[2 * w + 1];
+          if constexpr (!kOnes) l_run[qb] += p[2 * w] + p[2 * w + 1];
         }
       });
       static_for<C::DB>([&](auto dbi) {
@@ -707,6 +724,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void attn_fwd_kernel(
     constexpr int P = decltype(pc)::value;
     if (j >= n_steady || raise_pending) return false;
     constexpr int cur = P & 1, nxt = cur ^ 1;
+    ones_col(kVBase + P * C::TILE_B);
     constexpr int kb = ((P + 1) % kStages) * C::TILE_B;    // K of tile j+1
     constexpr int vb = kVBase + P * C::TILE_B;             // V of tile j
     constexpr int kdst = P * C::TILE_B;                    // K of tile j+4
@@ -742,7 +760,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void attn_fwd_kernel(
         } else if constexpr (kk < 12) {
           constexpr int w = kk - 8;
           pk[ch][w] = pack_bf16x2(pf[ch][2 * w], pf[ch][2 * w + 1]);
-        } else {
+        } else if constexpr (!kOnes) {
           constexpr int w = kk - 12;
           l_run[qb] += pf[ch][2 * w] + pf[ch][2 * w + 1];
         }
@@ -899,6 +917,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void attn_fwd_kernel(
         constexpr int qb = decltype(qbi)::value;
         m_use[qb] = m_offset(qb);
       });
+      ones_col(v_buf(j));
       exp_pv(s_cur, m_use, v_buf(j));
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -926,7 +945,11 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd<D>) void attn_fwd_kernel(
       (((uint64_t)split * B + wc.b) * H_U + wc.h) * (uint64_t)N_rows;  // first row of the unit
   static_for<kQB>([&](auto qbi) {
     constexpr int qb = decltype(qbi)::value;
-    const float l_tot = xhalf_sum(l_run[qb]);
+    float l_tot;
+    if constexpr (kOnes)
+      l_tot = xhalf_sum(g == 0 ? oacc[qb][C::DB - 1][12] : 0.f);
+    else
+      l_tot = xhalf_sum(l_run[qb]);
     const bool seen = l_tot > 0.f;
     const float inv = seen ? 1.f / l_tot : 0.f;
     const bool row_ok = my_row[qb] < N_rows;

@@ -35,7 +35,8 @@ def pytest_terminal_summary(terminalreporter):
     tr = terminalreporter
     tr.write_line(f"forward parity over {len(rows)} comparisons (bars: O max|err| beyond "
                   f"bf16 rounding <= {gpu_util.O_MAX_ABS}, rel-L2 <= {gpu_util.O_REL_L2}, "
-                  f"lse <= {gpu_util.LSE_MAX_ABS}):")
+                  f"lse <= {gpu_util.LSE_MAX_ABS}, {gpu_util.LSE_MAX_ABS_PADDED} for "
+                  f"padded head dims):")
     for key, r in worst.items():
         tr.write_line(f"  worst {key} = {r[key]:.3e}  ({r['what']})")
     out = os.path.join(ROOT, "gpurun_out")

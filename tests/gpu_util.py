@@ -6,6 +6,13 @@ error ||O_gpu - O_ref|| / ||O_ref|| <= 5e-3; lse max|err| <= 1e-3.  The
 expected error from rounding P to bf16 per tile and O to bf16 is about
 2.2e-3 relative L2, so the bar leaves a 2x margin.
 
+lse of a head dim below its padded width (d < 64, or 64 < d < 128): the row
+sum l is accumulated by the P V MFMA from the bf16-rounded P (the first
+element of V's padding chunk is set to 1), so each term of l carries the
+rounding of an 8-bit significand, a relative error of at most 2^-8, and
+|lse - lse_exact| <= ln(1 + 2^-8) = 3.9e-3.  The bar there is 4e-3, inside
+the output bar of max|err| <= 1e-2 that the method states.
+
 Reading of the max|err| bar: O is returned in bf16, whose own rounding is
 half an ulp of the value (up to 0.0156 at |O| in [4, 8)), which early causal
 rows reach because they average only a few V rows.  So each element's error
@@ -28,6 +35,12 @@ import torch
 O_MAX_ABS = 1e-2
 O_REL_L2 = 5e-3
 LSE_MAX_ABS = 1e-3
+LSE_MAX_ABS_PADDED = 4e-3
+
+
+def lse_bar(d: int) -> float:
+    """lse max|err| bar for head dim d (see the module docstring)."""
+    return LSE_MAX_ABS if d in (64, 128) else LSE_MAX_ABS_PADDED
 
 
 # Every forward comparison of this session: (what, raw max|err|, max|err|
@@ -69,7 +82,7 @@ def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
     assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
     assert max_abs <= O_MAX_ABS, f"{what}: O max|err| {max_abs}"
     assert rel <= O_REL_L2, f"{what}: O rel-L2 {rel}"
-    assert lse_err <= LSE_MAX_ABS, f"{what}: lse max|err| {lse_err}"
+    assert lse_err <= lse_bar(o_gpu.shape[-1]), f"{what}: lse max|err| {lse_err}"
     return max_abs, rel, lse_err
 
 
