@@ -61,10 +61,15 @@ def test_model_matches_measured_where_it_claims():
                 continue
             pred = 100 * l2model.predict_hit(B, H_Q, H_KV, N, d, causal, mode)
             meas = modes[name]["l2_hit_pct"]
-            # within 6 points: longest first, SHF non-causal, SBF at N >= 32K;
-            # the collapse of SHF under a causal mask at N = 128K with one
-            # workgroup per CU: both < 20%
-            if mode == 7 or (mode == 3 and not causal) or (mode == 2 and N >= 32768):
+            # within 6 points: longest first, SHF non-causal, SBF at N >= 32K
+            # with one workgroup per CU; SBF with two workgroups per CU
+            # (d <= 64): no reuse between workgroups predicted, and the
+            # measured rate stays below 10% (a floor of up to 7% from traffic
+            # the model leaves out); the collapse of SHF under a causal mask
+            # at N = 128K with one workgroup per CU: both < 20%
+            if mode == 2 and N >= 32768 and l2model.workgroups_per_cu(d) == 2:
+                assert pred == 0.0 and meas < 10.0, (workload, name, pred, meas)
+            elif mode == 7 or (mode == 3 and not causal) or (mode == 2 and N >= 32768):
                 assert abs(pred - meas) <= 6.0, (workload, name, pred, meas)
             elif mode == 3 and causal and N >= 131072 and l2model.workgroups_per_cu(d) == 1:
                 assert pred < 20.0 and meas < 20.0, (workload, name, pred, meas)
