@@ -81,22 +81,33 @@ SWEEP_MODES = (0, 1, 2, 3, 7, 15)
 PROFILE_MODES = SWEEP_MODES  # one dispatch each, in this order, per profile pass
 
 # Vector-ALU roofline of the online softmax.  Per (query, key) score the
-# softmax needs one FMA (scale, minus the running max), one exp2, one add
-# (row sum) and half a conversion to bf16 (two scores per instruction).  A
-# wave64 fp32 FMA, add or conversion issues in 4 SIMD cycles (16 lanes per
-# cycle: 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz = 78.6 TFLOP/s, half
-# the packed 157.3), v_exp_f32 in 8 (measured: two issue slots).  So one
-# wave's 64 scores take 4 + 8 + 4 + 4/2 = 18 SIMD cycles.
+# softmax needs one FMA (scale, minus the running max), one exp2, half a max3
+# (the tile max, two scores per instruction), half a conversion to bf16 (two
+# scores per instruction) and, where the head dim fills its padded width
+# (d = 64 or 128), one add for the row sum; below it the P V MFMA sums the
+# row through a 1 in V's padding.  A wave64 fp32 FMA, add, max3 or conversion
+# issues in 4 SIMD cycles (16 lanes per cycle: 256 CUs x 4 SIMDs x 16 lanes x
+# 2 FLOP x 2.4 GHz = 78.6 TFLOP/s, half the packed 157.3), v_exp_f32 in 8
+# (measured: two issue slots).  So one wave's 64 scores take
+# 4 + 8 + 2 + 2 (+ 4) = 16 (20) SIMD cycles.
 SIMDS = 256 * 4
 CLOCK_HZ = 2.4e9
-SOFTMAX_SIMD_CYCLES_PER_WAVE = {"fma": 4, "exp2": 8, "add": 4, "cvt_bf16_half": 2}
-SOFTMAX_SCORES_PER_S = SIMDS * CLOCK_HZ * 64 / sum(SOFTMAX_SIMD_CYCLES_PER_WAVE.values())
+SOFTMAX_SIMD_CYCLES_PER_WAVE = {"fma": 4, "exp2": 8, "max3_half": 2, "cvt_bf16_half": 2,
+                                "add": 4}
+
+
+def softmax_simd_cycles(d: int) -> int:
+    """SIMD cycles of softmax vector work per wave64 of scores at head dim d."""
+    c = dict(SOFTMAX_SIMD_CYCLES_PER_WAVE)
+    if d not in (64, 128):
+        del c["add"]
+    return sum(c.values())
 
 
 def alu_peak_tflops(d: int) -> float:
     """Credited TFLOP/s (4 d FLOP per score) at the softmax's vector-ALU
     bound."""
-    return SOFTMAX_SCORES_PER_S * 4 * d / 1e12
+    return SIMDS * CLOCK_HZ * 64 / softmax_simd_cycles(d) * 4 * d / 1e12
 
 
 def mfma_peak_tflops_credited(d: int) -> float:
@@ -1275,16 +1286,19 @@ def run_sweep(out_path: str):
 def _fwd_roofline(d: int, achieved: float, traffic):
     """The forward kernel's binding roofline: the MFMA peak (dense bf16,
     2.5 PFLOP/s) unless the softmax's vector-ALU bound is lower, as at
-    d <= 64 (d = 56: 1958 credited TFLOP/s against 2187 for the padded
-    MFMAs).  The other bound is reported beside it."""
+    d = 64 (2013 credited TFLOP/s against 2500).  At d = 56 the two nearly
+    meet (2202 against 2187 for the padded MFMAs).  The other bound is
+    reported beside it."""
     mfma = {"bound": "mfma", "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "achieved": round(achieved, 2), "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "peak_credited_at_padded_d": round(mfma_peak_tflops_credited(d), 1)}
     alu_peak = alu_peak_tflops(d)
     alu = {"bound": "alu", "peak": round(alu_peak, 1), "unit": "TFLOP/s (credited)",
            "achieved": round(achieved, 2), "frac": round(achieved / alu_peak, 4),
-           "derivation": "softmax vector work per score: fma 4 + exp2 8 + add 4 + half a bf16 "
-                         "conversion 2 SIMD cycles per wave64; 1024 SIMDs at 2.4 GHz"}
+           "derivation": f"softmax vector work per wave64 of scores: fma 4 + exp2 8 + half a "
+                         f"max3 2 + half a bf16 conversion 2"
+                         f"{' + row-sum add 4' if d in (64, 128) else ' (the row sum rides the P V MFMA)'}"
+                         f" = {softmax_simd_cycles(d)} SIMD cycles; 1024 SIMDs at 2.4 GHz"}
     if alu_peak < mfma_peak_tflops_credited(d):
         primary, other = alu, mfma
     else:
