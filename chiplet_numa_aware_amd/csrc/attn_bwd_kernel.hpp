@@ -47,8 +47,10 @@ constexpr int kBwdThreads = 256;
 constexpr int kBwdTile = 32;     // rows of a streamed tile
 
 // D = rowsum(dO * O) (fp32) and lse * log2(e), one wave per row; lane l owns
-// columns 2l, 2l+1.  ws holds [lse2 | D] of each (batch, query head), N
-// floats each.
+// columns 2l, 2l+1.  ws holds [lse2 | -D] of each (batch, query head), N
+// floats each: both gradient kernels start the accumulators of dP = dO V^T
+// from -D, so that the MFMAs return dP - D (the factor of dS = P (dP - D))
+// and the softmax gradient saves one subtraction per element.
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, float* __restrict__ ws, uint64_t rows, int d, int N) {
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(
   if (lane == 0) {
     const uint64_t head = row / (uint64_t)N, r = row - head * (uint64_t)N;
     ws[head * 2u * N + r] = lse[row] * 1.4426950408889634f;
-    ws[head * 2u * N + N + r] = acc;
+    ws[head * 2u * N + N + r] = -acc;  // -D: the dP accumulators start from it
   }
 }
 
@@ -223,6 +225,15 @@ struct DkvCfg {
   static_assert(BYTES <= 160 * 1024, "LDS");
   static_assert(kDkvStages * C::TILE_B <= 65536 - C::TILE_B, "stage offsets fit ds_read immediates");
 };
+
+// dP - D in one MFMA: the first 16-deep step of dP = dO V^T starts from the
+// rows' -D instead of 0.  The s_nop covers a VALU write of the C block (2
+// wait states before an XDL read of it).
+__device__ __forceinline__ void mfma_scores_from(f32x16& acc, const bf16x8& a, const bf16x8& b,
+                                                 const f32x16& c) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3"
+               : "=&v"(acc) : "v"(a), "a"(b), "v"(c));
+}
 
 // LDS-direct load of 4 bytes per lane: lane l writes LDS at M0 + 4 l.
 __device__ __forceinline__ void load_lds_dword(u32x4 desc, uint32_t voff, uint32_t m0) {
@@ -420,12 +431,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
       return *reinterpret_cast<const bf16x8*>(lb + sn * C::TILE_B + a);
     }
   };
-  auto read_stats = [&](int stage, f32x4 (&ls)[4], f32x4 (&ds)[4]) {
+  auto read_lse = [&](int stage, f32x4 (&ls)[4]) {
     static_for<4>([&](auto ci) {
       constexpr int c4 = decltype(ci)::value;
       ls[c4] = *reinterpret_cast<const f32x4*>(lb + st_addr + stage * L::ST_STAGE + 32 * c4);
-      ds[c4] = *reinterpret_cast<const f32x4*>(lb + st_addr + stage * L::ST_STAGE + 128 + 32 * c4);
     });
+  };
+  // The rows' -D as one block, element e = row 8 (e / 4) + 4 g + e % 4 (the
+  // accumulator order of dP).
+  auto read_negd = [&](int stage) {
+    f32x16 nd;
+    static_for<4>([&](auto ci) {
+      constexpr int c4 = decltype(ci)::value;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(lb + st_addr + stage * L::ST_STAGE + 128 + 32 * c4);
+      nd[4 * c4 + 0] = x[0];
+      nd[4 * c4 + 1] = x[1];
+      nd[4 * c4 + 2] = x[2];
+      nd[4 * c4 + 3] = x[3];
+    });
+    return nd;
   };
 
   f32x16 dk_acc[C::DB], dv_acc[C::DB];
@@ -443,13 +467,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
   wait_vmcnt<L::LPT>();
   barrier();
   f32x16 s_cur, dp_cur;
-  static_for<C::KC>([&](auto kci) {
-    constexpr int kc = decltype(kci)::value;
-    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(lb + row_q[kc]);
-    const bf16x8 da = *reinterpret_cast<const bf16x8*>(lb + row_do[kc]);
-    mfma_scores<(kc > 0)>(s_cur, qa, kf[kc]);
-    mfma_scores<(kc > 0)>(dp_cur, da, vf[kc]);
-  });
+  f32x4 lse4[4];
+  read_lse(0, lse4);
+  {
+    const f32x16 nd0 = read_negd(0);
+    static_for<C::KC>([&](auto kci) {
+      constexpr int kc = decltype(kci)::value;
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(lb + row_q[kc]);
+      const bf16x8 da = *reinterpret_cast<const bf16x8*>(lb + row_do[kc]);
+      mfma_scores<(kc > 0)>(s_cur, qa, kf[kc]);
+      if constexpr (kc == 0)
+        mfma_scores_from(dp_cur, da, vf[kc], nd0);
+      else
+        mfma_scores<true>(dp_cur, da, vf[kc]);
+    });
+  }
   uint32_t pk[8], dsk[8];
   static_for<8>([&](auto i) {
     pk[decltype(i)::value] = 0u;
@@ -459,8 +491,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
   static_for<L::AHEAD>([&](auto fi) {
     fr[decltype(fi)::value] = read_frag(std::integral_constant<int, 0>{}, fi);
   });
-  f32x4 lse4[4], dl4[4];
-  read_stats(0, lse4, dl4);
 
   // Causal / ragged mask of a lane's element (row 8 c4 + 4g + e of the tile):
   // visible iff lo <= row < hi, lo = the lane's key (causal) and hi = N (0 for
@@ -487,6 +517,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
     }
     bf16x8 frag[L::NF];
     static_for<L::AHEAD>([&](auto fi) { frag[decltype(fi)::value] = fr[decltype(fi)::value]; });
+    const f32x16 nd_nx = read_negd(s_next);  // -D of tile t+1, the C of its dP
     uint32_t pk_n[8], dsk_n[8];
     float p_e[16], ds_e[16];
     f32x16 s_nx, dp_nx;
@@ -508,7 +539,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
         if constexpr ((f - L::NA) % 2 == 0)
           mfma_scores<(kc > 0)>(s_nx, frag[f], kf[kc]);
         else
-          mfma_scores<(kc > 0)>(dp_nx, frag[f], vf[kc]);
+          if constexpr (kc == 0)
+            mfma_scores_from(dp_nx, frag[f], vf[kc], nd_nx);
+          else
+            mfma_scores<true>(dp_nx, frag[f], vf[kc]);
       }
       // The tile loads go out one per bundle, behind the MFMA.
       if constexpr (f < L::LPT) issue_one(lp, fi);
@@ -527,7 +561,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
           pin(dpv);
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, scale_log2, -lse4[c4][ee]));
           p_e[e] = p;
-          ds_e[e] = p * (dpv - dl4[c4][ee]);
+          ds_e[e] = p * dpv;  // dP - D
           if constexpr (e % 2 == 1) {
             pk_n[e / 2] = pack_bf16x2(p_e[e - 1], p_e[e]);
             dsk_n[e / 2] = pack_bf16x2(ds_e[e - 1], ds_e[e]);
@@ -543,7 +577,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
     static_for<L::AHEAD>([&](auto fi) {
       fr[decltype(fi)::value] = read_frag(std::integral_constant<int, (PH + 1) % kDkvStages>{}, fi);
     });
-    read_stats(s_next, lse4, dl4);
+    read_lse(s_next, lse4);
     static_for<8>([&](auto i) {
       pk[decltype(i)::value] = pk_n[decltype(i)::value];
       dsk[decltype(i)::value] = dsk_n[decltype(i)::value];
@@ -736,7 +770,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         s[kb][rb] = f32x4{};
-        dp[kb][rb] = f32x4{};
+        dp[kb][rb] = f32x4{drow[rb], drow[rb], drow[rb], drow[rb]};  // -D: dP - D
       }
 #pragma unroll
     for (int ds = 0; ds < kDS; ++ds)
@@ -771,7 +805,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(
                 const bool ok = key < N && rows[rb] < N && (!CAUSAL || key <= rows[rb]);
                 p = ok ? p : 0.f;
               }
-              ds2[e2] = p * (dp[kb][rb][e] - drow[rb]);
+              ds2[e2] = p * dp[kb][rb][e];
             }
             dsk[rb][kb * 2 + w] = pack_bf16x2(ds2[0], ds2[1]);
           }

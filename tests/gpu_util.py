@@ -23,7 +23,9 @@ The relative L2 bar is applied to the raw error.
 Backward (dQ, dK, dV): relative L2 error <= 1e-2 and max|err| <= 2e-2 *
 max|ref| per tensor, from the rounding steps of the kernels (bf16 P and dS
 before their products, D from the bf16 O, bf16 outputs): about 2.5e-3
-relative L2 is expected, so the bar leaves a 4x margin.
+relative L2 is expected, so the bar leaves a 4x margin.  Where the reference
+is identically zero, max|ref| gives way to a floor at the fp32 rounding of
+the cancelling terms (BWD_ZERO_REF_FLOOR).
 """
 from __future__ import annotations
 
@@ -88,6 +90,12 @@ def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
 
 BWD_REL_L2 = 1e-2
 BWD_MAX_REL = 2e-2
+# An identically zero reference gradient (dQ with one visible key: P = 1 and
+# dP = D, so dS = P (dP - D) vanishes exactly) leaves only the fp32 rounding
+# residue of the cancellation dP - D (about 2e-7 at d = 128); the max|err| bar
+# is relative to max|ref|, so it takes this floor in place of a zero max|ref|,
+# admitting 2e-2 x 5e-4 = 1e-5.
+BWD_ZERO_REF_FLOOR = 5e-4
 
 
 def check_grad(got, ref, what):
@@ -100,7 +108,8 @@ def check_grad(got, ref, what):
     mx = float(np.abs(err).max()) if err.size else 0.0
     say(f"  {what}: relL2={rel:.3e} max|err|={mx:.3e} (max|ref| {scale:.3e})")
     assert rel <= BWD_REL_L2, f"{what}: rel-L2 {rel}"
-    assert mx <= BWD_MAX_REL * max(scale, 1e-30), f"{what}: max|err| {mx} vs max|ref| {scale}"
+    assert mx <= BWD_MAX_REL * max(scale, BWD_ZERO_REF_FLOOR), \
+        f"{what}: max|err| {mx} vs max|ref| {scale}"
 
 
 def grad_inputs(B, H_Q, H_KV, N, d, seed):
