@@ -46,11 +46,16 @@ constexpr int kBwdBlock = 128;   // keys (dK/dV kernel) or rows (dQ kernel) per 
 constexpr int kBwdThreads = 256;
 constexpr int kBwdTile = 32;     // rows of a streamed tile
 
-// D = rowsum(dO * O) (fp32) and lse * log2(e), one wave per row; lane l owns
-// columns 2l, 2l+1.  ws holds [lse2 | -D] of each (batch, query head), N
-// floats each: both gradient kernels start the accumulators of dP = dO V^T
-// from -D, so that the MFMAs return dP - D (the factor of dS = P (dP - D))
-// and the softmax gradient saves one subtraction per element.
+// D = rowsum(dO * O) (fp32) and lse2 = lse * log2(e), one wave per row;
+// lane l owns columns 2l, 2l+1.  ws holds [-lse2 | -D] of each (batch, query
+// head), N floats each.  Both gradient kernels start their MFMA accumulators
+// from these: S from -lse2, with the operand held in registers (K in the
+// dK/dV kernel, Q in the dQ kernel) scaled once by log2(e) / sqrt(d) and
+// rounded to bf16, so the MFMAs return S log2(e) / sqrt(d) - lse2 and
+// P = exp2 of it with no FMA; dP = dO V^T from -D, so they return dP - D, the
+// factor of dS = P (dP - D), with no subtraction.  The scaled operand's
+// rounding adds about 1.7e-3 relative L2 to the gradients (2.4e-3 -> 3.0e-3
+// median on the parity cases).
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, float* __restrict__ ws, uint64_t rows, int d, int N) {
@@ -69,7 +74,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(
   for (int s = 32; s > 0; s >>= 1) acc += __shfl_xor(acc, s, 64);
   if (lane == 0) {
     const uint64_t head = row / (uint64_t)N, r = row - head * (uint64_t)N;
-    ws[head * 2u * N + r] = lse[row] * 1.4426950408889634f;
+    ws[head * 2u * N + r] = -lse[row] * 1.4426950408889634f;  // -lse2: S starts from it
     ws[head * 2u * N + N + r] = -acc;  // -D: the dP accumulators start from it
   }
 }
@@ -235,6 +240,16 @@ __device__ __forceinline__ void mfma_scores_from(f32x16& acc, const bf16x8& a, c
                : "=&v"(acc) : "v"(a), "a"(b), "v"(c));
 }
 
+// x * c for 8 bf16 values, rounded back to bf16 (nearest even).
+__device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8& x, float c) {
+  const u32x4 w = __builtin_bit_cast(u32x4, x);
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = pack_bf16x2(__uint_as_float(w[i] << 16) * c, __uint_as_float(w[i] & 0xFFFF0000u) * c);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // LDS-direct load of 4 bytes per lane: lane l writes LDS at M0 + 4 l.
 __device__ __forceinline__ void load_lds_dword(u32x4 desc, uint32_t voff, uint32_t m0) {
   asm volatile(
@@ -285,6 +300,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
     kf[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(k_rs, off, 0, 0));
     vf[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(v_rs, off, 0, 0));
   });
+  static_for<C::KC>([&](auto kci) { kf[decltype(kci)::value] = scale_bf16x8(kf[decltype(kci)::value], scale_log2); });
   static_for<C::KC>([&](auto kci) {
     xdl_guard_a(kf[decltype(kci)::value]);
     xdl_guard_a(vf[decltype(kci)::value]);
@@ -431,19 +447,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
       return *reinterpret_cast<const bf16x8*>(lb + sn * C::TILE_B + a);
     }
   };
-  auto read_lse = [&](int stage, f32x4 (&ls)[4]) {
-    static_for<4>([&](auto ci) {
-      constexpr int c4 = decltype(ci)::value;
-      ls[c4] = *reinterpret_cast<const f32x4*>(lb + st_addr + stage * L::ST_STAGE + 32 * c4);
-    });
-  };
-  // The rows' -D as one block, element e = row 8 (e / 4) + 4 g + e % 4 (the
-  // accumulator order of dP).
-  auto read_negd = [&](int stage) {
+  // A block of the stats of a tile: part 0 the rows' -lse2, part 128 their
+  // -D, element e = row 8 (e / 4) + 4 g + e % 4 (the accumulator order of
+  // S and dP).
+  auto read_block = [&](int stage, int part) {
     f32x16 nd;
     static_for<4>([&](auto ci) {
       constexpr int c4 = decltype(ci)::value;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(lb + st_addr + stage * L::ST_STAGE + 128 + 32 * c4);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(lb + st_addr + stage * L::ST_STAGE + part + 32 * c4);
       nd[4 * c4 + 0] = x[0];
       nd[4 * c4 + 1] = x[1];
       nd[4 * c4 + 2] = x[2];
@@ -467,15 +478,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
   wait_vmcnt<L::LPT>();
   barrier();
   f32x16 s_cur, dp_cur;
-  f32x4 lse4[4];
-  read_lse(0, lse4);
   {
-    const f32x16 nd0 = read_negd(0);
+    const f32x16 nl0 = read_block(0, 0), nd0 = read_block(0, 128);
     static_for<C::KC>([&](auto kci) {
       constexpr int kc = decltype(kci)::value;
       const bf16x8 qa = *reinterpret_cast<const bf16x8*>(lb + row_q[kc]);
       const bf16x8 da = *reinterpret_cast<const bf16x8*>(lb + row_do[kc]);
-      mfma_scores<(kc > 0)>(s_cur, qa, kf[kc]);
+      if constexpr (kc == 0)
+        mfma_scores_from(s_cur, qa, kf[kc], nl0);
+      else
+        mfma_scores<true>(s_cur, qa, kf[kc]);
       if constexpr (kc == 0)
         mfma_scores_from(dp_cur, da, vf[kc], nd0);
       else
@@ -517,7 +529,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
     }
     bf16x8 frag[L::NF];
     static_for<L::AHEAD>([&](auto fi) { frag[decltype(fi)::value] = fr[decltype(fi)::value]; });
-    const f32x16 nd_nx = read_negd(s_next);  // -D of tile t+1, the C of its dP
+    const f32x16 nl_nx = read_block(s_next, 0);    // -lse2 of tile t+1, the C of its S
+    const f32x16 nd_nx = read_block(s_next, 128);  // -D of tile t+1, the C of its dP
     uint32_t pk_n[8], dsk_n[8];
     float p_e[16], ds_e[16];
     f32x16 s_nx, dp_nx;
@@ -537,7 +550,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
       } else {
         constexpr int kc = (f - L::NA) / 2;
         if constexpr ((f - L::NA) % 2 == 0)
-          mfma_scores<(kc > 0)>(s_nx, frag[f], kf[kc]);
+          if constexpr (kc == 0)
+            mfma_scores_from(s_nx, frag[f], kf[kc], nl_nx);
+          else
+            mfma_scores<true>(s_nx, frag[f], kf[kc]);
         else
           if constexpr (kc == 0)
             mfma_scores_from(dp_nx, frag[f], vf[kc], nd_nx);
@@ -559,7 +575,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
           float sv = s_cur[e], dpv = dp_cur[e];
           pin(sv);
           pin(dpv);
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, scale_log2, -lse4[c4][ee]));
+          const float p = __builtin_amdgcn_exp2f(sv);  // S log2(e) / sqrt(d) - lse2
           p_e[e] = p;
           ds_e[e] = p * dpv;  // dP - D
           if constexpr (e % 2 == 1) {
@@ -577,7 +593,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkv_kernel(
     static_for<L::AHEAD>([&](auto fi) {
       fr[decltype(fi)::value] = read_frag(std::integral_constant<int, (PH + 1) % kDkvStages>{}, fi);
     });
-    read_lse(s_next, lse4);
     static_for<8>([&](auto i) {
       pk[decltype(i)::value] = pk_n[decltype(i)::value];
       dsk[decltype(i)::value] = dsk_n[decltype(i)::value];
@@ -703,7 +718,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(
     for (int ds = 0; ds < kDS; ++ds) {
       const int col = ds * 32 + q4 * 8;
       const uint32_t off = (FULL_D || col < dd) ? (uint32_t)(rows[rb] * dd + col) * 2u : kOutOfRange;
-      qf[rb][ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(q_rs, off, 0, 0));
+      qf[rb][ds] = scale_bf16x8(
+          __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(q_rs, off, 0, 0)), scale_log2);
       df[rb][ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(do_rs, off, 0, 0));
     }
     const uint64_t ridx = ((uint64_t)wc.b * H_Q + wc.h) * 2u * N + (rows[rb] < N ? rows[rb] : N - 1);
@@ -769,7 +785,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        s[kb][rb] = f32x4{};
+        s[kb][rb] = f32x4{lse2[rb], lse2[rb], lse2[rb], lse2[rb]};  // -lse2
         dp[kb][rb] = f32x4{drow[rb], drow[rb], drow[rb], drow[rb]};  // -D: dP - D
       }
 #pragma unroll
@@ -799,7 +815,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(
 #pragma unroll
             for (int e2 = 0; e2 < 2; ++e2) {
               const int e = 2 * w + e2;
-              float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][rb][e], scale_log2, -lse2[rb]));
+              float p = __builtin_amdgcn_exp2f(s[kb][rb][e]);
               if constexpr (MASKED) {
                 const int key = j * kBwdTile + kb * 16 + q4 * 4 + e;
                 const bool ok = key < N && rows[rb] < N && (!CAUSAL || key <= rows[rb]);

@@ -212,7 +212,7 @@ int attn_merge(const float* o_parts, const float* lse_parts, int num_splits,
  *   dq          device, bf16 [B][H_Q][N][d], written (every element)
  *   dk, dv      device, bf16 [B][H_KV][N][d], written (every element)
  *   ws          device, fp32 [B][H_Q][2][N], caller-owned workspace: per
- *               (batch, query head) lse * log2(e) of its rows, then -D
+ *               (batch, query head) -lse * log2(e) of its rows, then -D
  *               (minus rowsum(dO * O)); overwritten
  *   B, H_Q, H_KV, N, d, causal   as attn_fwd (the same mask); also
  *               B*H_Q*ceil(N/128) < 2^31
