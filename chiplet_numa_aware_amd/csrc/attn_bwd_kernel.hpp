@@ -224,9 +224,10 @@ struct DkvCfg {
   static constexpr int NB = 2 * C::KC;          // S and dP MFMAs of a tile
   static constexpr int NF = NA + NB;            // bundles per tile
   static constexpr int AHEAD = 4;               // operand fragments in flight
-  // Bundles over which P and dS of a tile are formed: the first part when it
-  // has 16 MFMAs (D = 128), else the whole tile.
-  static constexpr int NV = NA >= 16 ? NA : NF;
+  // Bundles over which P and dS of a tile are formed: the whole tile.  (With
+  // the accumulator starts that remove the FMA and the subtraction, keeping
+  // them in the first part at D = 128 measured 0.6-1.0% slower.)
+  static constexpr int NV = NF;
   static_assert(BYTES <= 160 * 1024, "LDS");
   static_assert(kDkvStages * C::TILE_B <= 65536 - C::TILE_B, "stage offsets fit ds_read immediates");
 };
