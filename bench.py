@@ -423,8 +423,8 @@ def _recorded_commands(directory: str, workload: str, which: str = "fwd"):
         import re
         with open(path) as f:
             # /root/repo is a link to wherever the run's copy of the
-            # repository lived; name the output paths through it
-            cmds = [re.sub(r"/\S*?/repo/gpurun_out/", "/root/repo/gpurun_out/", line.strip())
+            # repository lived; name its paths through it
+            cmds = [re.sub(r"/\S*?/repo/", "/root/repo/", line.strip())
                     for line in f if line.strip()]
         return dict(zip(profile_commands(workload, "X", which).keys(), cmds))
     return profile_commands(workload, os.path.abspath(directory), which)

@@ -20,8 +20,9 @@ def repo_root():
 
 def pytest_terminal_summary(terminalreporter):
     """Worst forward parity figures of the run, raw and beyond the bf16
-    output rounding, printed (also under -q) and written to
-    gpurun_out/parity_report.json when any forward comparison ran."""
+    output rounding, printed (also under -q) when any forward comparison
+    ran, and written as JSON to the path in ATTN_PARITY_REPORT when that is
+    set."""
     import json
     try:
         from tests import gpu_util
@@ -39,10 +40,12 @@ def pytest_terminal_summary(terminalreporter):
                   f"padded head dims):")
     for key, r in worst.items():
         tr.write_line(f"  worst {key} = {r[key]:.3e}  ({r['what']})")
-    out = os.path.join(ROOT, "gpurun_out")
+    path = os.environ.get("ATTN_PARITY_REPORT")
+    if not path:
+        return
     try:
-        os.makedirs(out, exist_ok=True)
-        with open(os.path.join(out, "parity_report.json"), "w") as f:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "w") as f:
             json.dump({"worst": {k: {"value": r[k], "case": r["what"]} for k, r in worst.items()},
                        "comparisons": rows}, f, indent=1)
     except OSError:
